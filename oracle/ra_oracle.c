@@ -1,0 +1,330 @@
+/*
+ * ra_oracle.c -- plain fp64 CPU oracle for the ring-attention hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  It shares no
+ * source with the HIP library and includes no HIP header.
+ *
+ * Pages cited (short names used below):
+ *   [P1] "Ring Attention如何让大模型突破百万token上下文：从环形通信到计算重叠的技术突围"
+ *        (answer.freetools.me blog post)
+ *   [P2] "Ring Attention with Blockwise Transformers for Near Infinite Context"
+ *        (reading notes on arXiv 2310.01889, papers.chlience.com)
+ *   [P3] aiqz.cc Ring Attention explainer (sections 分块注意力, 环状拓扑, 工程实现)
+ *
+ * What it computes is the plain definition, not the blocked algorithm:
+ *   - scaled dot-product attention softmax(Q K^T / sqrt(d)) V
+ *     ([P2] section 5.1, "基础 attention 语义"; [P3] 分块注意力 formula for S_b),
+ *     with d the head dimension;
+ *   - an explicit per-element causal mask: key token t_k is visible to query
+ *     token t_q iff t_k <= t_q ([P3] 工程实现: a token sees tokens whose index
+ *     does not exceed its own);
+ *   - token index of local row r on host h: contiguous h*c + r, striped r*N + h
+ *     ([P1] 因果掩码的负载均衡挑战, the striped device/token lists);
+ *   - the log-sum-exp of each row in natural-log units ([P1] Online Softmax,
+ *     LogSumExp form);
+ *   - the backward is the closed-form gradient of the same function (the pages
+ *     say only that the backward accumulates dQ, dK, dV along the ring,
+ *     [P2] section 5.2): with P = exp(S - LSE) on visible pairs,
+ *     D = rowsum(dO * O), dV = P^T dO, dS = P * (dO V^T - D),
+ *     dQ = scale * dS K, dK = scale * dS^T Q.
+ * Grouped heads: query head g reads key/value head g / (Hq / Hkv).
+ *
+ * Arrays are float32 in host-major layout [hosts][B][H][c][d]; every value
+ * is widened to double before use and every sum is accumulated in double.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_LAYOUT_CONTIGUOUS 0
+#define OR_LAYOUT_STRIPED 1
+
+/* Global token index of local row r on host h. */
+long long oracle_token_index(int layout, int n_hosts, long long block_len, int host,
+                             long long r)
+{
+    if (layout == OR_LAYOUT_STRIPED)
+        return r * (long long)n_hosts + host;
+    return (long long)host * block_len + r;
+}
+
+/* 1 if key token tk is visible to query token tq. */
+int oracle_visible(int causal, long long tq, long long tk)
+{
+    if (!causal)
+        return 1;
+    return tk <= tq ? 1 : 0;
+}
+
+/* Explicit mask of query block qhost against key block khost: out[r*c + r']. */
+void oracle_block_mask(int layout, int causal, int n_hosts, int block_len, int qhost,
+                       int khost, unsigned char *out)
+{
+    for (long long r = 0; r < block_len; ++r) {
+        long long tq = oracle_token_index(layout, n_hosts, block_len, qhost, r);
+        for (long long rk = 0; rk < block_len; ++rk) {
+            long long tk = oracle_token_index(layout, n_hosts, block_len, khost, rk);
+            out[r * block_len + rk] = (unsigned char)oracle_visible(causal, tq, tk);
+        }
+    }
+}
+
+typedef struct {
+    int n_hosts, batch, hq, hkv, c, d, layout, causal;
+    double scale;
+} or_dims;
+
+static size_t idx_row(const or_dims *g, int heads, int host, int b, int h, long long r)
+{
+    return ((((size_t)host * g->batch + b) * heads + h) * (size_t)g->c + (size_t)r) *
+           (size_t)g->d;
+}
+
+static double dot_f32(const float *a, const double *qd, int d)
+{
+    double s = 0.0;
+    for (int e = 0; e < d; ++e)
+        s += (double)a[e] * qd[e];
+    return s;
+}
+
+/* Forward for one query row.  q: the query vector (double).  Writes O[d],
+ * returns the max score in *mx, the denominator in *l and LSE. */
+static void fwd_row(const or_dims *g, const double *q, const float *K, const float *V,
+                    int qhost, long long r, int b, int kvh, double *O, double *mx_out,
+                    double *l_out, double *lse_out)
+{
+    const int d = g->d;
+    const long long tq = oracle_token_index(g->layout, g->n_hosts, g->c, qhost, r);
+    double mx = -INFINITY;
+    /* pass 1: row max over visible keys */
+    for (int j = 0; j < g->n_hosts; ++j)
+        for (long long rk = 0; rk < g->c; ++rk) {
+            long long tk = oracle_token_index(g->layout, g->n_hosts, g->c, j, rk);
+            if (!oracle_visible(g->causal, tq, tk))
+                continue;
+            double s = g->scale * dot_f32(K + idx_row(g, g->hkv, j, b, kvh, rk), q, d);
+            if (s > mx)
+                mx = s;
+        }
+    for (int e = 0; e < d; ++e)
+        O[e] = 0.0;
+    double l = 0.0;
+    if (mx == -INFINITY) {
+        *mx_out = mx;
+        *l_out = 0.0;
+        *lse_out = -INFINITY;
+        return;
+    }
+    /* pass 2: exp-sum and weighted sum of values */
+    for (int j = 0; j < g->n_hosts; ++j)
+        for (long long rk = 0; rk < g->c; ++rk) {
+            long long tk = oracle_token_index(g->layout, g->n_hosts, g->c, j, rk);
+            if (!oracle_visible(g->causal, tq, tk))
+                continue;
+            size_t o = idx_row(g, g->hkv, j, b, kvh, rk);
+            double p = exp(g->scale * dot_f32(K + o, q, d) - mx);
+            l += p;
+            const float *v = V + o;
+            for (int e = 0; e < d; ++e)
+                O[e] += p * (double)v[e];
+        }
+    for (int e = 0; e < d; ++e)
+        O[e] /= l;
+    *mx_out = mx;
+    *l_out = l;
+    *lse_out = mx + log(l);
+}
+
+/*
+ * Forward attention for a list of query rows.
+ *   Q: [n_q_hosts][B][Hq][c][d], host index h stored at h - q_host_base
+ *   (rows outside [q_host_base, q_host_base + n_q_hosts) are rejected)
+ *   K, V: [N][B][Hkv][c][d]
+ *   rows: n_rows x 4 int64 (host, batch, q_head, local row)
+ * Outputs (n_rows each; O is n_rows x d): O, LSE, max score, denominator.
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_attn_rows(const float *Q, const float *K, const float *V, int n_hosts,
+                     int batch, int hq, int hkv, int c, int d, int layout, int causal,
+                     double scale, int q_host_base, int n_q_hosts, long long n_rows,
+                     const long long *rows, double *O, double *lse, double *mx,
+                     double *l)
+{
+    if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || d <= 0 || c <= 0 || n_hosts <= 0)
+        return -1;
+    or_dims g = {n_hosts, batch, hq, hkv, c, d, layout, causal, scale};
+    const int group = hq / hkv;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long long i = 0; i < n_rows; ++i) {
+        const long long *rd = rows + 4 * i;
+        int host = (int)rd[0], b = (int)rd[1], h = (int)rd[2];
+        long long r = rd[3];
+        if (host < 0 || host >= n_hosts || host < q_host_base ||
+            host >= q_host_base + n_q_hosts || b < 0 || b >= batch || h < 0 || h >= hq ||
+            r < 0 || r >= c) {
+            bad = 1;
+            continue;
+        }
+        double *q = (double *)malloc(sizeof(double) * (size_t)d);
+        const float *qs = Q + idx_row(&g, hq, host - q_host_base, b, h, r);
+        for (int e = 0; e < d; ++e)
+            q[e] = (double)qs[e];
+        fwd_row(&g, q, K, V, host, r, b, h / group, O + (size_t)i * d, &mx[i], &l[i],
+                &lse[i]);
+        free(q);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Backward for a list of query rows: dQ (n_rows x d), plus the row's LSE and
+ * D = rowsum(dO * O) with O the oracle's own fp64 output.
+ *   dO: same layout and host base as Q.
+ */
+int oracle_attn_bwd_q_rows(const float *Q, const float *K, const float *V,
+                           const float *dO, int n_hosts, int batch, int hq, int hkv,
+                           int c, int d, int layout, int causal, double scale,
+                           int q_host_base, int n_q_hosts, long long n_rows,
+                           const long long *rows, double *dQ, double *lse_out,
+                           double *D_out)
+{
+    if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || d <= 0 || c <= 0 || n_hosts <= 0)
+        return -1;
+    or_dims g = {n_hosts, batch, hq, hkv, c, d, layout, causal, scale};
+    const int group = hq / hkv;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long long i = 0; i < n_rows; ++i) {
+        const long long *rd = rows + 4 * i;
+        int host = (int)rd[0], b = (int)rd[1], h = (int)rd[2];
+        long long r = rd[3];
+        if (host < 0 || host >= n_hosts || host < q_host_base ||
+            host >= q_host_base + n_q_hosts || b < 0 || b >= batch || h < 0 || h >= hq ||
+            r < 0 || r >= c) {
+            bad = 1;
+            continue;
+        }
+        const int kvh = h / group;
+        double *q = (double *)malloc(sizeof(double) * (size_t)d * 3);
+        double *o = q + d, *dov = q + 2 * d;
+        size_t qo = idx_row(&g, hq, host - q_host_base, b, h, r);
+        for (int e = 0; e < d; ++e) {
+            q[e] = (double)Q[qo + e];
+            dov[e] = (double)dO[qo + e];
+        }
+        double mxv, lv, lse;
+        fwd_row(&g, q, K, V, host, r, b, kvh, o, &mxv, &lv, &lse);
+        double D = 0.0;
+        for (int e = 0; e < d; ++e)
+            D += dov[e] * o[e];
+        double *dq = dQ + (size_t)i * d;
+        for (int e = 0; e < d; ++e)
+            dq[e] = 0.0;
+        const long long tq = oracle_token_index(layout, n_hosts, c, host, r);
+        if (lse != -INFINITY) {
+            for (int j = 0; j < n_hosts; ++j)
+                for (long long rk = 0; rk < c; ++rk) {
+                    long long tk = oracle_token_index(layout, n_hosts, c, j, rk);
+                    if (!oracle_visible(causal, tq, tk))
+                        continue;
+                    size_t ko = idx_row(&g, hkv, j, b, kvh, rk);
+                    double p = exp(scale * dot_f32(K + ko, q, d) - lse);
+                    double dp = dot_f32(V + ko, dov, d);
+                    double ds = p * (dp - D);
+                    for (int e = 0; e < d; ++e)
+                        dq[e] += scale * ds * (double)K[ko + e];
+                }
+        }
+        lse_out[i] = lse;
+        D_out[i] = D;
+        free(q);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Backward for a list of key rows: dK and dV (n_rows x d each).
+ *   rows: n_rows x 4 int64 (host, batch, kv_head, local row)
+ *   lse_all, D_all: [N][B][Hq][c] doubles for every query row of every host
+ *   (from the oracle's own forward); Q and dO hold all N hosts.
+ */
+int oracle_attn_bwd_kv_rows(const float *Q, const float *K, const float *V,
+                            const float *dO, const double *lse_all, const double *D_all,
+                            int n_hosts, int batch, int hq, int hkv, int c, int d,
+                            int layout, int causal, double scale, long long n_rows,
+                            const long long *rows, double *dK, double *dV)
+{
+    if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || d <= 0 || c <= 0 || n_hosts <= 0)
+        return -1;
+    or_dims g = {n_hosts, batch, hq, hkv, c, d, layout, causal, scale};
+    const int group = hq / hkv;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long long i = 0; i < n_rows; ++i) {
+        const long long *rd = rows + 4 * i;
+        int host = (int)rd[0], b = (int)rd[1], kvh = (int)rd[2];
+        long long rk = rd[3];
+        if (host < 0 || host >= n_hosts || b < 0 || b >= batch || kvh < 0 || kvh >= hkv ||
+            rk < 0 || rk >= c) {
+            bad = 1;
+            continue;
+        }
+        double *kv = (double *)malloc(sizeof(double) * (size_t)d * 2);
+        double *vv = kv + d;
+        size_t ko = idx_row(&g, hkv, host, b, kvh, rk);
+        for (int e = 0; e < d; ++e) {
+            kv[e] = (double)K[ko + e];
+            vv[e] = (double)V[ko + e];
+        }
+        double *dk = dK + (size_t)i * d, *dv = dV + (size_t)i * d;
+        for (int e = 0; e < d; ++e) {
+            dk[e] = 0.0;
+            dv[e] = 0.0;
+        }
+        const long long tk = oracle_token_index(layout, n_hosts, c, host, rk);
+        for (int h = kvh * group; h < (kvh + 1) * group; ++h)
+            for (int j = 0; j < n_hosts; ++j)
+                for (long long r = 0; r < c; ++r) {
+                    long long tq = oracle_token_index(layout, n_hosts, c, j, r);
+                    if (!oracle_visible(causal, tq, tk))
+                        continue;
+                    size_t qo = idx_row(&g, hq, j, b, h, r);
+                    size_t so = (((size_t)j * batch + b) * hq + h) * (size_t)c + (size_t)r;
+                    double lse = lse_all[so];
+                    if (lse == -INFINITY)
+                        continue;
+                    double p = exp(scale * dot_f32(Q + qo, kv, d) - lse);
+                    double dp = dot_f32(dO + qo, vv, d);
+                    double ds = p * (dp - D_all[so]);
+                    for (int e = 0; e < d; ++e) {
+                        dv[e] += p * (double)dO[qo + e];
+                        dk[e] += scale * ds * (double)Q[qo + e];
+                    }
+                }
+        free(kv);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Number of threads OpenMP will use (for reporting the CPU baseline). */
+int oracle_num_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        {
+#ifdef _OPENMP
+            n = omp_get_num_threads();
+#endif
+        }
+    }
+    return n;
+}

@@ -1,0 +1,193 @@
+"""Seeded synthetic inputs for the ring-attention workloads.
+
+This module is shared by the fp64 oracle (``oracle/``) and the HIP path
+(``long_context_transformers_amd``).  It holds no attention arithmetic: it
+only draws iid N(0, 1) samples from NumPy's PCG64, rounds them to bfloat16
+(round to nearest, ties to even), widens bfloat16 bit patterns back to
+float32 (exact), picks seeded row samples, and names the five workload
+shapes.
+
+Arrays are drawn directly in the host-major layout ``[N][B][H][c][d]``: block
+``h`` holds host ``h``'s share.  Which global token a local row ``r`` of host
+``h`` stands for is fixed by the token layout (contiguous or striped), which
+both sides compute on their own.  Because the samples are iid, drawing them in
+host-major order gives the same distribution as drawing a full sequence and
+permuting it.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+LAYOUT_CONTIGUOUS = 0
+LAYOUT_STRIPED = 1
+MASK_NONE = 0
+MASK_CAUSAL = 1
+DT_BF16 = 0
+DT_F32 = 1
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One workload shape.  ``hosts`` lists the simulated hosts that run."""
+
+    name: str
+    cfg: int                 # workload number, used to derive seeds
+    batch: int
+    heads_q: int
+    heads_kv: int
+    head_dim: int
+    n_hosts: int
+    block_len: int
+    dtype: int               # DT_BF16 or DT_F32
+    mask: int                # MASK_NONE or MASK_CAUSAL
+    layout: int              # LAYOUT_CONTIGUOUS or LAYOUT_STRIPED
+    host_begin: int
+    host_end: int
+    q_scale: float = 1.0     # multiplies Q before rounding (large-logit variant)
+    seed_offset: int = 0     # second seed set
+
+    @property
+    def seq_len(self) -> int:
+        return self.n_hosts * self.block_len
+
+    @property
+    def n_active(self) -> int:
+        return self.host_end - self.host_begin
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+def workloads() -> dict:
+    """The five workload shapes (b=1 everywhere)."""
+    w = {}
+    w["tiny"] = Workload("tiny_f32_noncausal_N4_c64", 1, 1, 2, 2, 64, 4, 64,
+                         DT_F32, MASK_NONE, LAYOUT_CONTIGUOUS, 0, 4)
+    w["tiny_bigq"] = w["tiny"].replace(name="tiny_f32_noncausal_N4_c64_qx8",
+                                       q_scale=8.0, seed_offset=100)
+    w["noncausal_32k"] = Workload("noncausal_32k_H8_d128_N8_c4096", 2, 1, 8, 8, 128,
+                                  8, 4096, DT_BF16, MASK_NONE,
+                                  LAYOUT_CONTIGUOUS, 0, 8)
+    w["causal_256k_contig"] = Workload("causal_256k_contiguous_H32_N8_c32768_host7",
+                                       3, 1, 32, 32, 128, 8, 32768, DT_BF16,
+                                       MASK_CAUSAL, LAYOUT_CONTIGUOUS, 7, 8)
+    w["causal_256k_striped"] = w["causal_256k_contig"].replace(
+        name="causal_256k_striped_H32_N8_c32768_host7", layout=LAYOUT_STRIPED)
+    w["striped_786k_gqa"] = Workload("striped_786k_gqa_Hq32_Hkv8_N16_c49152_host15",
+                                     4, 1, 32, 8, 128, 16, 49152, DT_BF16,
+                                     MASK_CAUSAL, LAYOUT_STRIPED, 15, 16)
+    w["bwd_64k"] = Workload("bwd_64k_causal_contiguous_H32_N8_c8192", 5, 1, 32, 32,
+                            128, 8, 8192, DT_BF16, MASK_CAUSAL,
+                            LAYOUT_CONTIGUOUS, 0, 8)
+    return w
+
+
+# ----------------------------------------------------------------------------
+# bfloat16 helpers (input quantisation only)
+# ----------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16, nearest-even; returns uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) & 0xFFFF
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns to float32 (exact)."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# seeded draws
+# ----------------------------------------------------------------------------
+
+def normal_f32(seed: int, shape, scale: float = 1.0) -> np.ndarray:
+    """iid N(0,1) float32 from PCG64(seed), optionally multiplied by ``scale``."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if scale != 1.0:
+        x = x * np.float32(scale)
+    return x
+
+
+def q_shape(w: Workload, hosts: Optional[int] = None):
+    n = w.n_hosts if hosts is None else hosts
+    return (n, w.batch, w.heads_q, w.block_len, w.head_dim)
+
+
+def kv_shape(w: Workload):
+    return (w.n_hosts, w.batch, w.heads_kv, w.block_len, w.head_dim)
+
+
+@dataclasses.dataclass
+class Inputs:
+    """Host-major inputs.  ``*_f32`` hold the exact values the device reads
+    (bf16 values widened to float32 for bf16 workloads)."""
+
+    q_f32: np.ndarray      # [N][B][Hq][c][d] (all N hosts)
+    k_f32: np.ndarray      # [N][B][Hkv][c][d]
+    v_f32: np.ndarray
+    q_dev: np.ndarray      # device representation: uint16 bf16 bits or float32
+    k_dev: np.ndarray
+    v_dev: np.ndarray
+    do_f32: Optional[np.ndarray] = None
+    do_dev: Optional[np.ndarray] = None
+
+
+def _quantise(w: Workload, x: np.ndarray):
+    if w.dtype == DT_BF16:
+        bits = f32_to_bf16_bits(x)
+        return bf16_bits_to_f32(bits), bits
+    return x, x
+
+
+def make_inputs(w: Workload, with_do: bool = False, q_hosts_only: bool = False) -> Inputs:
+    """Draw Q, K, V (and dO) for workload ``w``.
+
+    Seeds: Q = 1000 + cfg, K = 2000 + cfg, V = 3000 + cfg, dO = 4000 + cfg,
+    each plus ``seed_offset``.  With ``q_hosts_only`` only the active hosts'
+    Q blocks are kept (the draw itself is the same full-size stream)."""
+    so = w.seed_offset
+    q = normal_f32(1000 + w.cfg + so, q_shape(w), w.q_scale)
+    if q_hosts_only:
+        q = np.ascontiguousarray(q[w.host_begin:w.host_end])
+    k = normal_f32(2000 + w.cfg + so, kv_shape(w))
+    v = normal_f32(3000 + w.cfg + so, kv_shape(w))
+    qf, qd = _quantise(w, q)
+    del q
+    kf, kd = _quantise(w, k)
+    del k
+    vf, vd = _quantise(w, v)
+    del v
+    inp = Inputs(qf, kf, vf, qd, kd, vd)
+    if with_do:
+        do = normal_f32(4000 + w.cfg + so, q_shape(w))
+        if q_hosts_only:
+            do = np.ascontiguousarray(do[w.host_begin:w.host_end])
+        inp.do_f32, inp.do_dev = _quantise(w, do)
+    return inp
+
+
+def row_sample(w: Workload, n_rows: int = 1024, seed: Optional[int] = None) -> np.ndarray:
+    """Seeded sample of ``n_rows`` distinct local rows in [0, c), always
+    including rows 0, 1 and c-1; sorted."""
+    c = w.block_len
+    if n_rows >= c:
+        return np.arange(c, dtype=np.int64)
+    rng = np.random.default_rng(9000 + w.cfg if seed is None else seed)
+    fixed = {0, 1, c - 1}
+    pool = rng.choice(c, size=min(c, n_rows + 8), replace=False)
+    rows = list(fixed)
+    for p in pool:
+        if len(rows) >= n_rows:
+            break
+        if int(p) not in fixed:
+            rows.append(int(p))
+    return np.array(sorted(rows), dtype=np.int64)
