@@ -1,0 +1,369 @@
+#!/usr/bin/env python3
+"""Benchmark of the Ring Attention hot path on one MI355X.
+
+One step = one pass of the ring over one batch of synthetic input: the ring
+forward (scheduler, side-stream K/V transfers, block kernels, finalize) and,
+when the library provides it, the ring backward (preprocess, block backward
+kernels, K/V and dK/dV rotation), on the non-causal 32K workload: batch 1,
+8 heads, d = 128, 8 virtual hosts of c = 4096 tokens, bf16 inputs.
+
+Throughput is attention TFLOP/s counting only computed work: 4 d per visible
+(query, key) pair in the forward, 10 d in the backward ([P2] "Ring Attention
+with Blockwise Transformers for Near Infinite Context" reading notes, 5.4:
+4 d c^2 per block pair).  Inputs are resident in HBM before the timed region.
+
+Prints ONE JSON line.  Extra measurements (t_calc(c) sweep, causal and
+striped workloads, merge/finalize bandwidth) ride along under "extra".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import ra_synth as rs  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "ring-attention TFLOP/s per GPU (bf16, causal/striped) and % of MFMA peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def counted_pairs(w, host):
+    """Visible (query, key) pairs of one host's query block over the ring, per head."""
+    c, N = w.block_len, w.n_hosts
+    if w.mask == rs.MASK_NONE:
+        return N * c * c
+    if w.layout == rs.LAYOUT_CONTIGUOUS:
+        return host * c * c + c * (c + 1) // 2
+    return (host + 1) * c * (c + 1) // 2 + (N - 1 - host) * c * (c - 1) // 2
+
+
+def counted_flops(w, per_pair):
+    heads = w.batch * w.heads_q
+    return per_pair * w.head_dim * heads * sum(counted_pairs(w, h) for h in range(w.host_begin, w.host_end))
+
+
+class Ring:
+    """Device buffers and calls for one workload."""
+
+    def __init__(self, w, torch, ra, inp=None, seed=0, with_bwd=False):
+        self.w, self.torch, self.ra = w, torch, ra
+        dt = torch.bfloat16 if w.dtype == rs.DT_BF16 else torch.float32
+        na = w.n_active
+        if inp is not None:
+            def up(a):
+                return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+            q0 = w.host_begin - inp.q_host_base
+            self.q = up(inp.q_dev[q0:q0 + na])
+            self.k = up(inp.k_dev)
+            self.v = up(inp.v_dev)
+        else:
+            g = torch.Generator(device="cuda")
+            g.manual_seed(seed)
+            self.q = torch.randn(rs.q_shape(w, na), generator=g, device="cuda").to(dt)
+            self.k = torch.randn(rs.kv_shape(w), generator=g, device="cuda").to(dt)
+            self.v = torch.randn(rs.kv_shape(w), generator=g, device="cuda").to(dt)
+        self.O = torch.empty(rs.q_shape(w, na), dtype=dt, device="cuda")
+        self.lse = torch.empty((na, w.batch, w.heads_q, w.block_len), dtype=torch.float32, device="cuda")
+        self.dims = ra.Dims(w.batch, w.heads_q, w.heads_kv, w.head_dim, w.block_len, w.dtype)
+        cfg = ra.RingCfg(self.dims, w.n_hosts, w.host_begin, w.host_end, w.layout, w.mask)
+        self.ws = torch.empty(ra.ring_workspace_size(cfg), dtype=torch.uint8, device="cuda")
+        self.comm = torch.cuda.Stream()
+        self.with_bwd = with_bwd
+        if with_bwd:
+            g = torch.Generator(device="cuda")
+            g.manual_seed(seed + 1)
+            self.dO = torch.randn(rs.q_shape(w, na), generator=g, device="cuda").to(dt)
+            self.dQ = torch.empty(rs.q_shape(w, na), dtype=torch.float32, device="cuda")
+            self.dK = torch.empty(rs.kv_shape(w), dtype=torch.float32, device="cuda")
+            self.dV = torch.empty(rs.kv_shape(w), dtype=torch.float32, device="cuda")
+            self.wsb = torch.empty(ra.ring_workspace_size(cfg, True), dtype=torch.uint8, device="cuda")
+
+    def cfg(self, events=None):
+        w = self.w
+        return self.ra.RingCfg(self.dims, w.n_hosts, w.host_begin, w.host_end, w.layout, w.mask,
+                               step_events=events)
+
+    def fwd(self, events=None):
+        return self.ra.ring_fwd(self.cfg(events), self.q, self.k, self.v, self.O, self.lse, self.ws,
+                                self.torch.cuda.current_stream(), self.comm)
+
+    def bwd(self, events=None):
+        return self.ra.ring_bwd(self.cfg(events), self.q, self.k, self.v, self.O, self.lse, self.dO,
+                                self.dQ, self.dK, self.dV, self.wsb, self.torch.cuda.current_stream(),
+                                self.comm)
+
+
+def make_events(torch, n):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in ev:
+        e.record()
+    return ev
+
+
+def time_ring(ring, steps, warmup, bwd):
+    """Warm up, then time `steps` ring passes; per-launch kernel times from
+    the library's step events (recorded on the compute stream)."""
+    torch = ring.torch
+    N = ring.w.n_hosts
+    for _ in range(warmup):
+        ring.fwd()
+        if bwd:
+            ring.bwd()
+    torch.cuda.synchronize()
+    fev = [make_events(torch, 2 * N) for _ in range(steps)]
+    bev = [make_events(torch, 2 * N) for _ in range(steps)] if bwd else None
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        ring.fwd(fev[i])
+        if bwd:
+            ring.bwd(bev[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = start.elapsed_time(end)
+    f_ms = [fev[i][2 * s].elapsed_time(fev[i][2 * s + 1]) for i in range(steps) for s in range(N)]
+    b_ms = [bev[i][2 * s].elapsed_time(bev[i][2 * s + 1]) for i in range(steps) for s in range(N)] if bwd else []
+    return wall, gpu_ms, f_ms, b_ms
+
+
+def cpu_baseline(w, target_s=15.0):
+    """Time the fp64 oracle on a bounded sample of the workload's rows."""
+    from oracle import cref
+    inp = rs.make_inputs(w)
+    hosts = list(range(w.host_begin, w.host_end))
+
+    def run(n_rows):
+        rows = np.arange(n_rows) * (w.block_len // n_rows)
+        desc = cref.row_desc(hosts, range(w.batch), range(w.heads_q), rows)
+        t0 = time.perf_counter()
+        cref.attn_rows(inp.q_f32, inp.k_f32, inp.v_f32, n_hosts=w.n_hosts, layout=w.layout,
+                       causal=w.mask, rows=desc, q_host_base=inp.q_host_base)
+        dt = time.perf_counter() - t0
+        pairs = len(desc) * w.n_hosts * w.block_len   # non-causal: every key visible
+        return dt, pairs, len(desc)
+
+    dt, pairs, n = run(16)
+    n_rows = int(max(16, min(w.block_len, 16 * target_s / max(dt, 1e-3))))
+    n_rows = 16 * max(1, n_rows // 16)
+    if n_rows > 16:
+        dt, pairs, n = run(n_rows)
+    flops = 4.0 * w.head_dim * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cref.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n} query rows ({n_rows} evenly spaced rows x {w.heads_q} heads x "
+                      f"{len(hosts)} hosts) of {w.name}, fp64, {dt:.1f} s wall"}
+
+
+def tcalc_sweep(torch, ra, reps=5):
+    """t_calc(c): one FULL and one TRI_INCL block through ra_block_fwd, H=32, d=128."""
+    out = {}
+    for c in (512, 1024, 2048, 4096, 8192, 16384, 32768):
+        dims = ra.Dims(1, 32, 32, 128, c, rs.DT_BF16)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(c)
+        q = torch.randn((1, 32, c, 128), generator=g, device="cuda").to(torch.bfloat16)
+        k = torch.randn((1, 32, c, 128), generator=g, device="cuda").to(torch.bfloat16)
+        v = torch.randn((1, 32, c, 128), generator=g, device="cuda").to(torch.bfloat16)
+        m = torch.empty((1, 32, c), dtype=torch.float32, device="cuda")
+        l = torch.empty_like(m)
+        O = torch.empty((1, 32, c, 128), dtype=torch.float32, device="cuda")
+        res = {}
+        for cls, qoff in (("full", c), ("tri_incl", 0)):
+            ra.state_init(dims, m, l, O)
+            ts = []
+            for r in range(reps + 2):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                ra.block_fwd(dims, q, k, v, ra.RA_MASK_CAUSAL, qoff, 0, 1, m, l, O)
+                b.record()
+                b.synchronize()
+                if r >= 2:
+                    ts.append(a.elapsed_time(b))
+            med = statistics.median(ts) / 1e3
+            pairs = c * c if cls == "full" else c * (c + 1) // 2
+            res[cls] = {"t_calc_s": med, "tflops": 4 * 128 * 32 * pairs / med / 1e12}
+        out[c] = res
+        del q, k, v, m, l, O
+    # overlap crossing: smallest c with t_calc(c) >= t_comm(c) = 4 c d H_kv / B
+    cross = {}
+    for name, B in (("xgmi_153GBs", 153e9), ("nvlink_300GBs", 300e9), ("ib_12.5GBs", 12.5e9)):
+        tc = {c: v["full"]["t_calc_s"] for c, v in out.items()}
+        cross[name] = ra.overlap.crossing_block_len(tc, 32, 128, B)
+    f_meas = max(v["full"]["tflops"] for v in out.values()) * 1e12
+    return {"t_calc": {str(c): v for c, v in out.items()},
+            "crossing_c": cross,
+            "F_meas_over_B": {"153GBs": f_meas / 153e9, "300GBs": f_meas / 300e9, "12.5GBs": f_meas / 12.5e9}}
+
+
+def elementwise_bw(torch, ra, reps=10):
+    """Finalize and merge at one 256K-host shape (32 heads, c = 32768, d = 128)."""
+    B, Hq, c, d = 1, 32, 32768, 128
+    dims = ra.Dims(B, Hq, Hq, d, c, rs.DT_BF16)
+    rows = B * Hq * c
+    m = torch.randn((B, Hq, c), device="cuda")
+    l = torch.rand((B, Hq, c), device="cuda") + 1
+    O = torch.randn((B, Hq, c, d), device="cuda")
+    Ob = torch.empty((B, Hq, c, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq, c), device="cuda")
+    O2 = torch.randn_like(O)
+    l2 = torch.randn_like(m)
+    Om = torch.empty_like(O)
+    lm = torch.empty_like(m)
+
+    def timeit(fn):
+        fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) / reps / 1e3
+
+    tf = timeit(lambda: ra.finalize(dims, m, l, O, Ob, lse))
+    tm = timeit(lambda: ra.merge_lse(dims, O, m, O2, l2, Om, lm))
+    fin_bytes = rows * (6 * d + 12)     # O fp32 read, m, l read, bf16 out, lse out
+    mer_bytes = rows * (12 * d + 12)    # two fp32 O in, one out, three lse
+    return {"finalize": {"s": tf, "GBs": fin_bytes / tf / 1e9, "bytes_per_row": 6 * d + 12},
+            "merge": {"s": tm, "GBs": mer_bytes / tm / 1e9, "bytes_per_row": 12 * d + 12},
+            "peak_GBs": PEAK_HBM_GBS}
+
+
+def causal_rates(torch, ra, steps=3):
+    """Forward TFLOP/s of the causal 256K host-7 workload in both layouts and
+    of the 786K striped GQA host-15 workload (seeded device-side inputs)."""
+    out = {}
+    wl = rs.workloads()
+    for key in ("causal_256k_contig", "causal_256k_striped", "striped_786k_gqa"):
+        w = wl[key]
+        ring = Ring(w, torch, ra, seed=w.cfg)
+        ring.fwd()
+        torch.cuda.synchronize()
+        wall, gpu_ms, f_ms, _ = time_ring(ring, steps, 0, False)
+        fl = counted_flops(w, 4)
+        active = [t for t in f_ms if t > 0.01]
+        out[key] = {"ms": gpu_ms / steps, "tflops": fl / (gpu_ms / steps / 1e3) / 1e12,
+                    "kernel_ms_per_step": sum(f_ms) / steps}
+        del ring
+        torch.cuda.empty_cache()
+    nc = None
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-bwd", action="store_true", help="time the ring forward only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU: the N virtual hosts of the ring share it; "
+                                   "--gpus above 1 is not supported", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import long_context_transformers_amd as ra
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ra.version()
+
+    w = rs.workloads()["noncausal_32k"]
+    log(f"[bench] workload {w.name}: drawing inputs")
+    inp = rs.make_inputs(w)
+    bwd = not args.no_bwd
+    ring = Ring(w, torch, ra, inp=inp, with_bwd=True)
+    if bwd:
+        try:
+            ring.fwd()
+            ring.bwd()
+            torch.cuda.synchronize()
+        except ra.RingAttnError as e:
+            log(f"[bench] ring backward unavailable ({e}); timing the forward only")
+            bwd = False
+    log(f"[bench] timing {args.steps} steps after {args.warmup} warm-up steps (backward: {bwd})")
+    wall, gpu_ms, f_ms, b_ms = time_ring(ring, args.steps, args.warmup, bwd)
+    ms_per_step = wall * 1e3 / args.steps
+    fwd_flops = counted_flops(w, 4)
+    bwd_flops = counted_flops(w, 10) if bwd else 0
+    value = (fwd_flops + bwd_flops) / (ms_per_step / 1e3) / 1e12
+
+    # dominant kernel: the block kernel with the most total time per step
+    N = w.n_hosts
+    f_launch = statistics.mean(f_ms)
+    b_launch = statistics.mean(b_ms) if bwd else 0.0
+    if b_launch * 1 > f_launch:
+        dom = {"kernel": "block backward (dK/dV + dQ kernels of one ring step, all hosts)",
+               "flops_per_launch": bwd_flops / N, "avg_launch_ms": b_launch}
+    else:
+        dom = {"kernel": "fwd_bf16_kernel (one ring step, all 8 hosts)",
+               "flops_per_launch": fwd_flops / N, "avg_launch_ms": f_launch}
+    achieved = dom["flops_per_launch"] / (dom["avg_launch_ms"] / 1e3) / 1e12
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "kernel": dom["kernel"], "avg_launch_ms": dom["avg_launch_ms"],
+                "algorithmic_flops_per_launch": dom["flops_per_launch"]}
+
+    extra = {"fwd_tflops": fwd_flops / (sum(f_ms) / args.steps / 1e3) / 1e12,
+             "fwd_kernel_avg_launch_ms": f_launch,
+             "fwd_kernel_tflops": (fwd_flops / N) / (f_launch / 1e3) / 1e12,
+             "gpu_event_ms_per_step": gpu_ms / args.steps}
+    if bwd:
+        extra["bwd_kernel_avg_launch_ms"] = b_launch
+        extra["bwd_step_tflops"] = (bwd_flops / N) / (b_launch / 1e3) / 1e12
+    if not args.no_extra:
+        log("[bench] causal / striped workloads")
+        extra["causal"] = causal_rates(torch, ra)
+        nc_rate = extra["fwd_kernel_tflops"]
+        st = extra["causal"]["causal_256k_striped"]["tflops"]
+        extra["striped_vs_noncausal_per_flop"] = st / nc_rate
+        log("[bench] t_calc(c) sweep")
+        extra["overlap"] = tcalc_sweep(torch, ra)
+        log("[bench] finalize / merge bandwidth")
+        extra["elementwise"] = elementwise_bw(torch, ra)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (fp64 oracle)")
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name + (" ring fwd+bwd" if bwd else " ring fwd"), "global_batch": w.batch,
+                   "seq_len": w.seq_len, "heads": w.heads_q, "head_dim": w.head_dim,
+                   "virtual_hosts": w.n_hosts, "block_len": w.block_len,
+                   "parallelism": "ring of 8 virtual hosts on 1 GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -45,8 +45,8 @@
 #define OR_LAYOUT_STRIPED 1
 
 /* Global token index of local row r on host h. */
-long long oracle_token_index(int layout, int n_hosts, long long block_len, int host,
-                             long long r)
+static inline long long token_index(int layout, int n_hosts, long long block_len, int host,
+                                    long long r)
 {
     if (layout == OR_LAYOUT_STRIPED)
         return r * (long long)n_hosts + host;
@@ -54,11 +54,22 @@ long long oracle_token_index(int layout, int n_hosts, long long block_len, int h
 }
 
 /* 1 if key token tk is visible to query token tq. */
-int oracle_visible(int causal, long long tq, long long tk)
+static inline int visible(int causal, long long tq, long long tk)
 {
     if (!causal)
         return 1;
     return tk <= tq ? 1 : 0;
+}
+
+long long oracle_token_index(int layout, int n_hosts, long long block_len, int host,
+                             long long r)
+{
+    return token_index(layout, n_hosts, block_len, host, r);
+}
+
+int oracle_visible(int causal, long long tq, long long tk)
+{
+    return visible(causal, tq, tk);
 }
 
 /* Explicit mask of query block qhost against key block khost: out[r*c + r']. */
@@ -66,10 +77,10 @@ void oracle_block_mask(int layout, int causal, int n_hosts, int block_len, int q
                        int khost, unsigned char *out)
 {
     for (long long r = 0; r < block_len; ++r) {
-        long long tq = oracle_token_index(layout, n_hosts, block_len, qhost, r);
+        long long tq = token_index(layout, n_hosts, block_len, qhost, r);
         for (long long rk = 0; rk < block_len; ++rk) {
-            long long tk = oracle_token_index(layout, n_hosts, block_len, khost, rk);
-            out[r * block_len + rk] = (unsigned char)oracle_visible(causal, tq, tk);
+            long long tk = token_index(layout, n_hosts, block_len, khost, rk);
+            out[r * block_len + rk] = (unsigned char)visible(causal, tq, tk);
         }
     }
 }
@@ -77,6 +88,7 @@ void oracle_block_mask(int layout, int causal, int n_hosts, int block_len, int q
 typedef struct {
     int n_hosts, batch, hq, hkv, c, d, layout, causal;
     double scale;
+    const float *K, *V;
 } or_dims;
 
 static size_t idx_row(const or_dims *g, int heads, int host, int b, int h, long long r)
@@ -85,30 +97,55 @@ static size_t idx_row(const or_dims *g, int heads, int host, int b, int h, long 
            (size_t)g->d;
 }
 
+/* Dot product in double.  The definition fixes no summation order; the SIMD
+ * reduction lets the compiler split the sum across vector lanes. */
+/* Dot product of two double vectors; 16 partial sums (any order is allowed). */
+static double dot_d(const double *a, const double *b, int d)
+{
+    double acc[16] = {0.0};
+    int e = 0;
+    for (; e + 16 <= d; e += 16)
+        for (int u = 0; u < 16; ++u)
+            acc[u] += a[e + u] * b[e + u];
+    double s = 0.0;
+    for (; e < d; ++e)
+        s += a[e] * b[e];
+    for (int u = 0; u < 16; ++u)
+        s += acc[u];
+    return s;
+}
+
+#define K_ROW(g, j, b, kvh, rk) ((g)->K + idx_row((g), (g)->hkv, (j), (b), (kvh), (rk)))
+#define V_ROW(g, j, b, kvh, rk) ((g)->V + idx_row((g), (g)->hkv, (j), (b), (kvh), (rk)))
+
 static double dot_f32(const float *a, const double *qd, int d)
 {
     double s = 0.0;
+#pragma omp simd reduction(+ : s)
     for (int e = 0; e < d; ++e)
         s += (double)a[e] * qd[e];
     return s;
 }
 
-/* Forward for one query row.  q: the query vector (double).  Writes O[d],
- * returns the max score in *mx, the denominator in *l and LSE. */
+/* Forward for one query row.  q: the query vector (double); sc: scratch of
+ * N*c doubles for the row's scores.  Writes O[d], the max score, the
+ * denominator and LSE. */
 static void fwd_row(const or_dims *g, const double *q, const float *K, const float *V,
-                    int qhost, long long r, int b, int kvh, double *O, double *mx_out,
-                    double *l_out, double *lse_out)
+                    int qhost, long long r, int b, int kvh, double *sc, double *O,
+                    double *mx_out, double *l_out, double *lse_out)
 {
     const int d = g->d;
-    const long long tq = oracle_token_index(g->layout, g->n_hosts, g->c, qhost, r);
+    const long long c = g->c;
+    const long long tq = token_index(g->layout, g->n_hosts, c, qhost, r);
     double mx = -INFINITY;
-    /* pass 1: row max over visible keys */
+    /* scores of the visible keys, and their max */
     for (int j = 0; j < g->n_hosts; ++j)
-        for (long long rk = 0; rk < g->c; ++rk) {
-            long long tk = oracle_token_index(g->layout, g->n_hosts, g->c, j, rk);
-            if (!oracle_visible(g->causal, tq, tk))
+        for (long long rk = 0; rk < c; ++rk) {
+            long long tk = token_index(g->layout, g->n_hosts, c, j, rk);
+            if (!visible(g->causal, tq, tk))
                 continue;
             double s = g->scale * dot_f32(K + idx_row(g, g->hkv, j, b, kvh, rk), q, d);
+            sc[j * c + rk] = s;
             if (s > mx)
                 mx = s;
         }
@@ -121,16 +158,16 @@ static void fwd_row(const or_dims *g, const double *q, const float *K, const flo
         *lse_out = -INFINITY;
         return;
     }
-    /* pass 2: exp-sum and weighted sum of values */
+    /* exp-sum and weighted sum of values */
     for (int j = 0; j < g->n_hosts; ++j)
-        for (long long rk = 0; rk < g->c; ++rk) {
-            long long tk = oracle_token_index(g->layout, g->n_hosts, g->c, j, rk);
-            if (!oracle_visible(g->causal, tq, tk))
+        for (long long rk = 0; rk < c; ++rk) {
+            long long tk = token_index(g->layout, g->n_hosts, c, j, rk);
+            if (!visible(g->causal, tq, tk))
                 continue;
-            size_t o = idx_row(g, g->hkv, j, b, kvh, rk);
-            double p = exp(g->scale * dot_f32(K + o, q, d) - mx);
+            double p = exp(sc[j * c + rk] - mx);
             l += p;
-            const float *v = V + o;
+            const float *v = V + idx_row(g, g->hkv, j, b, kvh, rk);
+#pragma omp simd
             for (int e = 0; e < d; ++e)
                 O[e] += p * (double)v[e];
         }
@@ -139,6 +176,82 @@ static void fwd_row(const or_dims *g, const double *q, const float *K, const flo
     *mx_out = mx;
     *l_out = l;
     *lse_out = mx + log(l);
+}
+
+/* Up to OR_SET query rows of one (host, batch, head) are evaluated in one
+ * sweep over the keys, so each key/value row is read once per set instead of
+ * once per query row.  Every row's arithmetic is exactly fwd_row's. */
+#define OR_SET 16
+
+static void fwd_rowset(const or_dims *g, int nset, const double *const *q, const long long *r,
+                       int qhost, int b, int kvh, double *const *sc, double *const *O,
+                       double *mx, double *l, double *lse)
+{
+    const int d = g->d;
+    const long long c = g->c;
+    long long tq[OR_SET];
+    double kd[512];
+    for (int i = 0; i < nset; ++i) {
+        tq[i] = token_index(g->layout, g->n_hosts, c, qhost, r[i]);
+        mx[i] = -INFINITY;
+        l[i] = 0.0;
+        for (int e = 0; e < d; ++e)
+            O[i][e] = 0.0;
+    }
+    /* scores of the visible keys, and each row's max */
+    for (int j = 0; j < g->n_hosts; ++j)
+        for (long long rk = 0; rk < c; ++rk) {
+            long long tk = token_index(g->layout, g->n_hosts, c, j, rk);
+            const float *k = K_ROW(g, j, b, kvh, rk);
+            int any = 0;
+            for (int i = 0; i < nset; ++i)
+                any |= visible(g->causal, tq[i], tk);
+            if (!any)
+                continue;
+            for (int e = 0; e < d; ++e)
+                kd[e] = (double)k[e];
+            for (int i = 0; i < nset; ++i) {
+                if (!visible(g->causal, tq[i], tk))
+                    continue;
+                double s = g->scale * dot_d(kd, q[i], d);
+                sc[i][j * c + rk] = s;
+                if (s > mx[i])
+                    mx[i] = s;
+            }
+        }
+    /* exp-sum and weighted sum of values */
+    for (int j = 0; j < g->n_hosts; ++j)
+        for (long long rk = 0; rk < c; ++rk) {
+            long long tk = token_index(g->layout, g->n_hosts, c, j, rk);
+            const float *v = V_ROW(g, j, b, kvh, rk);
+            int any = 0;
+            for (int i = 0; i < nset; ++i)
+                any |= visible(g->causal, tq[i], tk);
+            if (!any)
+                continue;
+            for (int e = 0; e < d; ++e)
+                kd[e] = (double)v[e];
+            for (int i = 0; i < nset; ++i) {
+                if (!visible(g->causal, tq[i], tk))
+                    continue;
+                double p = exp(sc[i][j * c + rk] - mx[i]);
+                l[i] += p;
+                double *oi = O[i];
+#pragma omp simd
+                for (int e = 0; e < d; ++e)
+                    oi[e] += p * kd[e];
+            }
+        }
+    for (int i = 0; i < nset; ++i) {
+        if (mx[i] == -INFINITY) {
+            lse[i] = -INFINITY;
+            l[i] = 0.0;
+            continue;
+        }
+        for (int e = 0; e < d; ++e)
+            O[i][e] /= l[i];
+        lse[i] = mx[i] + log(l[i]);
+    }
 }
 
 /*
@@ -156,31 +269,59 @@ int oracle_attn_rows(const float *Q, const float *K, const float *V, int n_hosts
                      const long long *rows, double *O, double *lse, double *mx,
                      double *l)
 {
-    if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || d <= 0 || c <= 0 || n_hosts <= 0)
+    if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || d <= 0 || d > 512 || c <= 0 || n_hosts <= 0)
         return -1;
-    or_dims g = {n_hosts, batch, hq, hkv, c, d, layout, causal, scale};
+    or_dims g = {n_hosts, batch, hq, hkv, c, d, layout, causal, scale, K, V};
     const int group = hq / hkv;
-    int bad = 0;
-#pragma omp parallel for schedule(dynamic, 1)
     for (long long i = 0; i < n_rows; ++i) {
         const long long *rd = rows + 4 * i;
         int host = (int)rd[0], b = (int)rd[1], h = (int)rd[2];
         long long r = rd[3];
         if (host < 0 || host >= n_hosts || host < q_host_base ||
             host >= q_host_base + n_q_hosts || b < 0 || b >= batch || h < 0 || h >= hq ||
-            r < 0 || r >= c) {
-            bad = 1;
-            continue;
-        }
-        double *q = (double *)malloc(sizeof(double) * (size_t)d);
-        const float *qs = Q + idx_row(&g, hq, host - q_host_base, b, h, r);
-        for (int e = 0; e < d; ++e)
-            q[e] = (double)qs[e];
-        fwd_row(&g, q, K, V, host, r, b, h / group, O + (size_t)i * d, &mx[i], &l[i],
-                &lse[i]);
-        free(q);
+            r < 0 || r >= c)
+            return -1;
     }
-    return bad ? -1 : 0;
+    /* sets: runs of up to OR_SET consecutive rows with the same (host, batch, head) */
+    long long *set_start = (long long *)malloc(sizeof(long long) * (size_t)(n_rows + 1));
+    long long n_sets = 0;
+    for (long long i = 0; i < n_rows;) {
+        long long j = i + 1;
+        while (j < n_rows && j - i < OR_SET && rows[4 * j] == rows[4 * i] &&
+               rows[4 * j + 1] == rows[4 * i + 1] && rows[4 * j + 2] == rows[4 * i + 2])
+            ++j;
+        set_start[n_sets++] = i;
+        i = j;
+    }
+    set_start[n_sets] = n_rows;
+#pragma omp parallel
+    {
+        double *buf = (double *)malloc(sizeof(double) * (size_t)OR_SET *
+                                       ((size_t)d + (size_t)n_hosts * c));
+#pragma omp for schedule(dynamic, 1)
+        for (long long s = 0; s < n_sets; ++s) {
+            const long long i0 = set_start[s];
+            const int nset = (int)(set_start[s + 1] - i0);
+            const long long *rd = rows + 4 * i0;
+            const int host = (int)rd[0], b = (int)rd[1], h = (int)rd[2];
+            double *qp[OR_SET], *scp[OR_SET], *op[OR_SET];
+            long long rr[OR_SET];
+            for (int i = 0; i < nset; ++i) {
+                qp[i] = buf + (size_t)i * d;
+                scp[i] = buf + (size_t)OR_SET * d + (size_t)i * n_hosts * c;
+                op[i] = O + (size_t)(i0 + i) * d;
+                rr[i] = rows[4 * (i0 + i) + 3];
+                const float *qs = Q + idx_row(&g, hq, host - q_host_base, b, h, rr[i]);
+                for (int e = 0; e < d; ++e)
+                    qp[i][e] = (double)qs[e];
+            }
+            fwd_rowset(&g, nset, (const double *const *)qp, rr, host, b, h / group,
+                       (double *const *)scp, (double *const *)op, mx + i0, l + i0, lse + i0);
+        }
+        free(buf);
+    }
+    free(set_start);
+    return 0;
 }
 
 /*
@@ -197,7 +338,7 @@ int oracle_attn_bwd_q_rows(const float *Q, const float *K, const float *V,
 {
     if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || d <= 0 || c <= 0 || n_hosts <= 0)
         return -1;
-    or_dims g = {n_hosts, batch, hq, hkv, c, d, layout, causal, scale};
+    or_dims g = {n_hosts, batch, hq, hkv, c, d, layout, causal, scale, K, V};
     const int group = hq / hkv;
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -212,32 +353,33 @@ int oracle_attn_bwd_q_rows(const float *Q, const float *K, const float *V,
             continue;
         }
         const int kvh = h / group;
-        double *q = (double *)malloc(sizeof(double) * (size_t)d * 3);
-        double *o = q + d, *dov = q + 2 * d;
+        double *q = (double *)malloc(sizeof(double) * ((size_t)d * 3 + (size_t)n_hosts * c));
+        double *o = q + d, *dov = q + 2 * d, *sc = q + 3 * d;
         size_t qo = idx_row(&g, hq, host - q_host_base, b, h, r);
         for (int e = 0; e < d; ++e) {
             q[e] = (double)Q[qo + e];
             dov[e] = (double)dO[qo + e];
         }
         double mxv, lv, lse;
-        fwd_row(&g, q, K, V, host, r, b, kvh, o, &mxv, &lv, &lse);
+        fwd_row(&g, q, K, V, host, r, b, kvh, sc, o, &mxv, &lv, &lse);
         double D = 0.0;
         for (int e = 0; e < d; ++e)
             D += dov[e] * o[e];
         double *dq = dQ + (size_t)i * d;
         for (int e = 0; e < d; ++e)
             dq[e] = 0.0;
-        const long long tq = oracle_token_index(layout, n_hosts, c, host, r);
+        const long long tq = token_index(layout, n_hosts, c, host, r);
         if (lse != -INFINITY) {
             for (int j = 0; j < n_hosts; ++j)
                 for (long long rk = 0; rk < c; ++rk) {
-                    long long tk = oracle_token_index(layout, n_hosts, c, j, rk);
-                    if (!oracle_visible(causal, tq, tk))
+                    long long tk = token_index(layout, n_hosts, c, j, rk);
+                    if (!visible(causal, tq, tk))
                         continue;
                     size_t ko = idx_row(&g, hkv, j, b, kvh, rk);
-                    double p = exp(scale * dot_f32(K + ko, q, d) - lse);
+                    double p = exp(sc[(long long)j * c + rk] - lse);
                     double dp = dot_f32(V + ko, dov, d);
                     double ds = p * (dp - D);
+#pragma omp simd
                     for (int e = 0; e < d; ++e)
                         dq[e] += scale * ds * (double)K[ko + e];
                 }
@@ -263,7 +405,7 @@ int oracle_attn_bwd_kv_rows(const float *Q, const float *K, const float *V,
 {
     if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || d <= 0 || c <= 0 || n_hosts <= 0)
         return -1;
-    or_dims g = {n_hosts, batch, hq, hkv, c, d, layout, causal, scale};
+    or_dims g = {n_hosts, batch, hq, hkv, c, d, layout, causal, scale, K, V};
     const int group = hq / hkv;
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -288,12 +430,12 @@ int oracle_attn_bwd_kv_rows(const float *Q, const float *K, const float *V,
             dk[e] = 0.0;
             dv[e] = 0.0;
         }
-        const long long tk = oracle_token_index(layout, n_hosts, c, host, rk);
+        const long long tk = token_index(layout, n_hosts, c, host, rk);
         for (int h = kvh * group; h < (kvh + 1) * group; ++h)
             for (int j = 0; j < n_hosts; ++j)
                 for (long long r = 0; r < c; ++r) {
-                    long long tq = oracle_token_index(layout, n_hosts, c, j, r);
-                    if (!oracle_visible(causal, tq, tk))
+                    long long tq = token_index(layout, n_hosts, c, j, r);
+                    if (!visible(causal, tq, tk))
                         continue;
                     size_t qo = idx_row(&g, hq, j, b, h, r);
                     size_t so = (((size_t)j * batch + b) * hq + h) * (size_t)c + (size_t)r;
@@ -303,6 +445,7 @@ int oracle_attn_bwd_kv_rows(const float *Q, const float *K, const float *V,
                     double p = exp(scale * dot_f32(Q + qo, kv, d) - lse);
                     double dp = dot_f32(dO + qo, vv, d);
                     double ds = p * (dp - D_all[so]);
+#pragma omp simd
                     for (int e = 0; e < d; ++e) {
                         dv[e] += p * (double)dO[qo + e];
                         dk[e] += scale * ds * (double)Q[qo + e];

@@ -108,9 +108,10 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 # seeded draws
 # ----------------------------------------------------------------------------
 
-def normal_f32(seed: int, shape, scale: float = 1.0) -> np.ndarray:
-    """iid N(0,1) float32 from PCG64(seed), optionally multiplied by ``scale``."""
-    rng = np.random.default_rng(seed)
+def normal_f32(seed, shape, scale: float = 1.0) -> np.ndarray:
+    """iid N(0,1) float32 from PCG64(seed) (seed: int or tuple of ints),
+    optionally multiplied by ``scale``."""
+    rng = np.random.default_rng(list(seed) if isinstance(seed, tuple) else seed)
     x = rng.standard_normal(size=shape, dtype=np.float32)
     if scale != 1.0:
         x = x * np.float32(scale)
@@ -122,56 +123,64 @@ def q_shape(w: Workload, hosts: Optional[int] = None):
     return (n, w.batch, w.heads_q, w.block_len, w.head_dim)
 
 
-def kv_shape(w: Workload):
-    return (w.n_hosts, w.batch, w.heads_kv, w.block_len, w.head_dim)
+def kv_shape(w: Workload, hosts: Optional[int] = None):
+    n = w.n_hosts if hosts is None else hosts
+    return (n, w.batch, w.heads_kv, w.block_len, w.head_dim)
 
 
 @dataclasses.dataclass
 class Inputs:
     """Host-major inputs.  ``*_f32`` hold the exact values the device reads
-    (bf16 values widened to float32 for bf16 workloads)."""
+    (bf16 values widened to float32 for bf16 workloads); ``*_dev`` hold the
+    device representation (uint16 bf16 bit patterns, or float32).
+    ``q_*`` / ``do_*`` cover hosts [q_host_base, q_host_base + len)."""
 
-    q_f32: np.ndarray      # [N][B][Hq][c][d] (all N hosts)
-    k_f32: np.ndarray      # [N][B][Hkv][c][d]
+    q_f32: np.ndarray
+    k_f32: np.ndarray
     v_f32: np.ndarray
-    q_dev: np.ndarray      # device representation: uint16 bf16 bits or float32
+    q_dev: np.ndarray
     k_dev: np.ndarray
     v_dev: np.ndarray
+    q_host_base: int = 0
     do_f32: Optional[np.ndarray] = None
     do_dev: Optional[np.ndarray] = None
 
 
-def _quantise(w: Workload, x: np.ndarray):
-    if w.dtype == DT_BF16:
-        bits = f32_to_bf16_bits(x)
-        return bf16_bits_to_f32(bits), bits
-    return x, x
+def _draw_blocks(w: Workload, base_seed: int, hosts, shape_one, scale: float = 1.0):
+    """Blocks of the given hosts; block h is drawn from seed (base_seed, h).
+    Returns (exact float32 values, device representation)."""
+    n = len(hosts)
+    f = np.empty((n,) + shape_one, dtype=np.float32)
+    dev = np.empty((n,) + shape_one, dtype=np.uint16 if w.dtype == DT_BF16 else np.float32)
+    for i, h in enumerate(hosts):
+        x = normal_f32((base_seed, h), shape_one, scale)
+        if w.dtype == DT_BF16:
+            bits = f32_to_bf16_bits(x)
+            dev[i] = bits
+            f[i] = bf16_bits_to_f32(bits)
+        else:
+            dev[i] = x
+            f[i] = x
+    return f, dev
 
 
 def make_inputs(w: Workload, with_do: bool = False, q_hosts_only: bool = False) -> Inputs:
     """Draw Q, K, V (and dO) for workload ``w``.
 
-    Seeds: Q = 1000 + cfg, K = 2000 + cfg, V = 3000 + cfg, dO = 4000 + cfg,
-    each plus ``seed_offset``.  With ``q_hosts_only`` only the active hosts'
-    Q blocks are kept (the draw itself is the same full-size stream)."""
+    Block h of each tensor comes from PCG64 seeded with (base + cfg +
+    seed_offset, h), base = 1000 (Q), 2000 (K), 3000 (V), 4000 (dO).  K and V
+    cover all N hosts; Q and dO cover the active hosts only when
+    ``q_hosts_only`` (else all N)."""
     so = w.seed_offset
-    q = normal_f32(1000 + w.cfg + so, q_shape(w), w.q_scale)
-    if q_hosts_only:
-        q = np.ascontiguousarray(q[w.host_begin:w.host_end])
-    k = normal_f32(2000 + w.cfg + so, kv_shape(w))
-    v = normal_f32(3000 + w.cfg + so, kv_shape(w))
-    qf, qd = _quantise(w, q)
-    del q
-    kf, kd = _quantise(w, k)
-    del k
-    vf, vd = _quantise(w, v)
-    del v
-    inp = Inputs(qf, kf, vf, qd, kd, vd)
+    qh = list(range(w.host_begin, w.host_end)) if q_hosts_only else list(range(w.n_hosts))
+    one_q = q_shape(w, 1)[1:]
+    one_kv = kv_shape(w, 1)[1:]
+    qf, qd = _draw_blocks(w, 1000 + w.cfg + so, qh, one_q, w.q_scale)
+    kf, kd = _draw_blocks(w, 2000 + w.cfg + so, range(w.n_hosts), one_kv)
+    vf, vd = _draw_blocks(w, 3000 + w.cfg + so, range(w.n_hosts), one_kv)
+    inp = Inputs(qf, kf, vf, qd, kd, vd, q_host_base=qh[0])
     if with_do:
-        do = normal_f32(4000 + w.cfg + so, q_shape(w))
-        if q_hosts_only:
-            do = np.ascontiguousarray(do[w.host_begin:w.host_end])
-        inp.do_f32, inp.do_dev = _quantise(w, do)
+        inp.do_f32, inp.do_dev = _draw_blocks(w, 4000 + w.cfg + so, qh, one_q)
     return inp
 
 

@@ -1,0 +1,235 @@
+"""Host-side logic of libringattn, checked on the CPU (no GPU calls).
+
+- every function include/ringattn.h declares is exported by the library;
+- the ring schedule (source block, class and offsets per step) is bit-exact
+  against the oracle's explicit per-element masks;
+- printed examples: ring holdings, striped token lists, block counts;
+- argument checks fail before any HIP call;
+- the c >= F/B reporter against the pages' table.
+"""
+import ctypes
+import json
+import os
+import re
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import long_context_transformers_amd as ra
+from long_context_transformers_amd import _lib as L
+from oracle import cref
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+C, S = ra.RA_LAYOUT_CONTIGUOUS, ra.RA_LAYOUT_STRIPED
+
+
+def test_header_symbols_exported():
+    hdr = open(os.path.join(ROOT, "include", "ringattn.h")).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(ra_[a-z_0-9]+)\s*\(", hdr, re.M))
+    assert len(declared) >= 17, declared
+    lib = L.load()
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert declared == {n for n, _, _ in L.SIGNATURES}
+
+
+def _implied_mask(step, c, mask):
+    r = np.arange(c)[:, None]
+    rk = np.arange(c)[None, :]
+    if mask == ra.RA_MASK_NONE:
+        return np.ones((c, c), dtype=bool)
+    return step["kv_offset"] + rk * step["stride"] <= step["q_offset"] + r * step["stride"]
+
+
+_CLASS_PATTERN = {
+    ra.RA_BLK_FULL: lambda c: np.ones((c, c), dtype=bool),
+    ra.RA_BLK_SKIP: lambda c: np.zeros((c, c), dtype=bool),
+    ra.RA_BLK_TRI_INCL: lambda c: np.tril(np.ones((c, c), dtype=bool)),
+    ra.RA_BLK_TRI_STRICT: lambda c: np.tril(np.ones((c, c), dtype=bool), -1),
+}
+
+
+@pytest.mark.parametrize("layout", [C, S])
+@pytest.mark.parametrize("mask", [ra.RA_MASK_NONE, ra.RA_MASK_CAUSAL])
+def test_schedule_bit_exact_vs_oracle_masks(layout, mask):
+    for N in (1, 2, 3, 4, 5, 8, 16):
+        for c in (2, 3, 8, 64):
+            for i in range(N):
+                steps = ra.schedule(N, i, c, layout, mask)
+                assert [s["src"] for s in steps] == [(i - s) % N for s in range(N)]
+                for s in steps:
+                    want = cref.block_mask(layout, mask, N, c, i, s["src"]).astype(bool)
+                    got = _implied_mask(s, c, mask)
+                    assert np.array_equal(got, want), (layout, mask, N, c, i, s)
+                    assert np.array_equal(_CLASS_PATTERN[s["cls"]](c), want), (N, c, i, s)
+
+
+def test_schedule_ring_holdings(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "ring_holdings_N4.json")))
+    for step, held in g["held"].items():
+        for host, blk in enumerate(held):
+            assert ra.schedule(4, host, 16, C, ra.RA_MASK_NONE)[int(step)]["src"] == blk
+
+
+def test_schedule_block_counts(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "contiguous_split_4dev_100tok.json")))
+    N, c = g["n_hosts"], g["block_len"]
+    for i in range(N):
+        steps = ra.schedule(N, i, c, C, ra.RA_MASK_CAUSAL)
+        live = [s for s in steps if s["cls"] != ra.RA_BLK_SKIP]
+        assert len(live) * c == g["attention_shape"][str(i)][1]
+        # N compute steps including the host's own block, own block first
+        assert steps[0]["src"] == i and steps[0]["cls"] == ra.RA_BLK_TRI_INCL
+    for i in range(N):
+        steps = ra.schedule(N, i, c, S, ra.RA_MASK_CAUSAL)
+        assert all(s["cls"] in (ra.RA_BLK_TRI_INCL, ra.RA_BLK_TRI_STRICT) for s in steps)
+
+
+def test_token_index_golden(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "striped_tokens_N4.json")))
+    for dev, toks in g["tokens_per_device_prefix"].items():
+        assert [ra.token_index(S, 4, 100, int(dev), r) for r in range(4)] == toks
+    for h in range(5):
+        for r in (0, 1, 6):
+            assert ra.token_index(C, 5, 7, h, r) == cref.token_index(C, 5, 7, h, r)
+            assert ra.token_index(S, 5, 7, h, r) == cref.token_index(S, 5, 7, h, r)
+    assert ra.token_index(S, 4, 10, 4, 0) == -1 and ra.token_index(C, 4, 10, 0, 10) == -1
+
+
+def test_block_class_general_offsets():
+    # a band: key row r' visible iff r' - r <= 5
+    assert ra.block_class_of(ra.RA_MASK_CAUSAL, 5, 0, 1, 64) == ra.RA_BLK_BAND
+    assert ra.block_class_of(ra.RA_MASK_CAUSAL, 0, 64, 1, 64) == ra.RA_BLK_SKIP
+    assert ra.block_class_of(ra.RA_MASK_CAUSAL, 63, 0, 1, 64) == ra.RA_BLK_FULL
+    assert ra.block_class_of(ra.RA_MASK_CAUSAL, 0, 63, 1, 64) == ra.RA_BLK_BAND
+    assert ra.block_class_of(ra.RA_MASK_CAUSAL, 0, 64, 1, 64) == ra.RA_BLK_SKIP
+    # striped: floor division for negative offsets
+    assert ra.block_class_of(ra.RA_MASK_CAUSAL, 2, 3, 4, 8) == ra.RA_BLK_TRI_STRICT
+    assert ra.block_class_of(ra.RA_MASK_CAUSAL, 3, 2, 4, 8) == ra.RA_BLK_TRI_INCL
+    # c = 1: the diagonal block is a single visible pair
+    assert ra.block_class_of(ra.RA_MASK_CAUSAL, 0, 0, 1, 1) == ra.RA_BLK_FULL
+    assert ra.block_class_of(ra.RA_MASK_NONE, 0, 99, 1, 8) == ra.RA_BLK_FULL
+    assert ra.block_class_of(ra.RA_MASK_CAUSAL, 0, 0, 0, 8) == -1
+
+
+# ---------------------------------------------------------------------------
+# argument checks: every call below has a bad argument and must fail before
+# any HIP call (fake device addresses are never dereferenced)
+# ---------------------------------------------------------------------------
+
+FAKE = 0x10000          # aligned, never touched
+MIS = 0x10004           # misaligned
+
+
+def _dims(**kw):
+    d = dict(batch=1, heads_q=4, heads_kv=2, head_dim=128, block_len=64, dtype=0, scale=0.0)
+    d.update(kw)
+    return L.RaDims(**d)
+
+
+def _call_block_fwd(dims, q=FAKE, k=FAKE, v=FAKE, mask=0, stride=1, m=FAKE, l=FAKE, o=FAKE):
+    return ra.raw_call("ra_block_fwd", ctypes.byref(dims), q, k, v, mask, 0, 0, stride, m, l, o, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(heads_q=3, heads_kv=2), L.RA_ERR_INVALID_ARG),
+    (dict(head_dim=96), L.RA_ERR_UNSUPPORTED),
+    (dict(block_len=0), L.RA_ERR_INVALID_ARG),
+    (dict(batch=0), L.RA_ERR_INVALID_ARG),
+    (dict(dtype=7), L.RA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), L.RA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), L.RA_ERR_INVALID_ARG),
+])
+def test_bad_dims(kw, expect):
+    assert _call_block_fwd(_dims(**kw)) == expect
+    assert ra.last_error()
+
+
+def test_bad_pointers_and_modes():
+    d = _dims()
+    assert _call_block_fwd(d, q=None) == L.RA_ERR_INVALID_ARG
+    assert _call_block_fwd(d, k=MIS) == L.RA_ERR_INVALID_ARG and "aligned" in ra.last_error()
+    assert _call_block_fwd(d, mask=5) == L.RA_ERR_INVALID_ARG
+    assert _call_block_fwd(d, stride=0) == L.RA_ERR_INVALID_ARG
+    assert ra.raw_call("ra_merge_lse", ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == L.RA_ERR_INVALID_ARG
+    assert ra.raw_call("ra_finalize", ctypes.byref(d), FAKE, FAKE, FAKE, MIS, FAKE, None) == L.RA_ERR_INVALID_ARG
+    assert ra.raw_call("ra_bwd_preprocess", ctypes.byref(d), FAKE, None, FAKE, None) == L.RA_ERR_INVALID_ARG
+    assert ra.raw_call("ra_state_init", None, FAKE, FAKE, FAKE, None) == L.RA_ERR_INVALID_ARG
+    assert ra.raw_call("ra_layout_permute", ctypes.byref(d), 2, 4, 0, 1, FAKE, FAKE, None) == L.RA_ERR_INVALID_ARG
+    assert ra.raw_call("ra_layout_permute", ctypes.byref(d), 2, 4, 9, 1, FAKE, FAKE + 256, None) == L.RA_ERR_INVALID_ARG
+    assert ra.raw_call("ra_mask_tile", 0, 0, 0, 4, 4, FAKE, None) == L.RA_ERR_INVALID_ARG
+    assert ra.raw_call("ra_block_bwd", ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 0, 1,
+                       FAKE, FAKE, None, None) == L.RA_ERR_INVALID_ARG
+    out = (L.RaStep * 4)()
+    assert ra.raw_call("ra_schedule", 4, 4, 8, 0, 1, out) == L.RA_ERR_INVALID_ARG
+    assert ra.raw_call("ra_schedule", 4, 0, 8, 3, 1, out) == L.RA_ERR_INVALID_ARG
+    assert ra.raw_call("ra_schedule", 4, 0, 8, 0, 1, None) == L.RA_ERR_INVALID_ARG
+
+
+def _cfg(**kw):
+    c = dict(dims=_dims(), n_hosts=8, host_begin=0, host_end=8, layout=0, mask=0, flags=0,
+             debug_copy_delay_us=0)
+    c.update(kw)
+    return L.RaRingCfg(**c)
+
+
+def _ring_fwd(cfg, ws_bytes, ws=0x100000):
+    st = L.RaRingStats()
+    return ra.raw_call("ra_ring_fwd", ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, FAKE, ws, ws_bytes,
+                       None, None, ctypes.byref(st))
+
+
+def test_ring_argument_checks():
+    cfg = _cfg()
+    n = ctypes.c_size_t(0)
+    assert ra.raw_call("ra_ring_workspace_size", ctypes.byref(cfg), 0, ctypes.byref(n)) == 0
+    need = n.value
+    assert _ring_fwd(cfg, need - 1) == L.RA_ERR_WORKSPACE
+    assert _ring_fwd(cfg, need, ws=0x100010) == L.RA_ERR_INVALID_ARG   # not 256-aligned
+    assert _ring_fwd(_cfg(host_begin=3, host_end=3), need) == L.RA_ERR_INVALID_ARG
+    assert _ring_fwd(_cfg(host_end=9), need) == L.RA_ERR_INVALID_ARG
+    assert _ring_fwd(_cfg(layout=2), need) == L.RA_ERR_INVALID_ARG
+    assert _ring_fwd(_cfg(flags=0x80), need) == L.RA_ERR_INVALID_ARG
+    assert _ring_fwd(_cfg(n_hosts=0), need) == L.RA_ERR_INVALID_ARG
+    st = L.RaRingStats()
+    # backward: partial host ranges are not supported
+    assert ra.raw_call("ra_ring_bwd", ctypes.byref(_cfg(host_begin=7)), *([FAKE] * 10), 1 << 40,
+                       None, None, ctypes.byref(st)) == L.RA_ERR_UNSUPPORTED
+
+
+def test_workspace_size_formula():
+    # per simulated host: m, l (fp32 rows), O (fp32), 2 slots x (K, V) blocks
+    d = _dims(batch=1, heads_q=8, heads_kv=8, head_dim=128, block_len=4096)
+    cfg = _cfg(dims=d)
+    n = ctypes.c_size_t(0)
+    assert ra.raw_call("ra_ring_workspace_size", ctypes.byref(cfg), 0, ctypes.byref(n)) == 0
+    rows = 8 * 4096
+    want = 8 * (2 * rows * 4 + rows * 128 * 4 + 4 * 8 * 4096 * 128 * 2)
+    assert n.value == want
+    cfg1 = _cfg(dims=d, host_begin=7, host_end=8)
+    assert ra.raw_call("ra_ring_workspace_size", ctypes.byref(cfg1), 0, ctypes.byref(n)) == 0
+    assert n.value == want // 8
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    code = ("import long_context_transformers_amd._lib as L; L.LIB_PATH='/nonexistent/libringattn.so';\n"
+            "try:\n L.load()\nexcept ImportError as e:\n print('raised', e)\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert "raised" in out.stdout
+
+
+def test_overlap_threshold_table(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "min_block_size_table.json")))
+    tol = g["tolerance_rel"]
+    for row in g["rows"]:
+        F = row["flops"] * 1e12
+        B = row["bandwidth"] * 1e9
+        c = ra.overlap.min_block_size(F, B)
+        assert abs(c / 1000 - row["min_block"]) <= tol * row["min_block"] + 0.05, row
+        assert abs(ra.overlap.min_local_sequence(F, B) / 1000 - row["min_seq"]) <= tol * row["min_seq"], row
+    # the time model: a block pair's 4 d c^2 FLOPs against 4 c d bytes
+    assert ra.overlap.block_flops(128, 1024) == 4 * 128 * 1024 ** 2
+    assert ra.overlap.kv_transfer_bytes(128, 1024) == 4 * 1024 * 128
+    assert ra.overlap.ring_time(8, 2.0, 3.0) == 24.0
