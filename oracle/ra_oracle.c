@@ -127,57 +127,6 @@ static double dot_f32(const float *a, const double *qd, int d)
     return s;
 }
 
-/* Forward for one query row.  q: the query vector (double); sc: scratch of
- * N*c doubles for the row's scores.  Writes O[d], the max score, the
- * denominator and LSE. */
-static void fwd_row(const or_dims *g, const double *q, const float *K, const float *V,
-                    int qhost, long long r, int b, int kvh, double *sc, double *O,
-                    double *mx_out, double *l_out, double *lse_out)
-{
-    const int d = g->d;
-    const long long c = g->c;
-    const long long tq = token_index(g->layout, g->n_hosts, c, qhost, r);
-    double mx = -INFINITY;
-    /* scores of the visible keys, and their max */
-    for (int j = 0; j < g->n_hosts; ++j)
-        for (long long rk = 0; rk < c; ++rk) {
-            long long tk = token_index(g->layout, g->n_hosts, c, j, rk);
-            if (!visible(g->causal, tq, tk))
-                continue;
-            double s = g->scale * dot_f32(K + idx_row(g, g->hkv, j, b, kvh, rk), q, d);
-            sc[j * c + rk] = s;
-            if (s > mx)
-                mx = s;
-        }
-    for (int e = 0; e < d; ++e)
-        O[e] = 0.0;
-    double l = 0.0;
-    if (mx == -INFINITY) {
-        *mx_out = mx;
-        *l_out = 0.0;
-        *lse_out = -INFINITY;
-        return;
-    }
-    /* exp-sum and weighted sum of values */
-    for (int j = 0; j < g->n_hosts; ++j)
-        for (long long rk = 0; rk < c; ++rk) {
-            long long tk = token_index(g->layout, g->n_hosts, c, j, rk);
-            if (!visible(g->causal, tq, tk))
-                continue;
-            double p = exp(sc[j * c + rk] - mx);
-            l += p;
-            const float *v = V + idx_row(g, g->hkv, j, b, kvh, rk);
-#pragma omp simd
-            for (int e = 0; e < d; ++e)
-                O[e] += p * (double)v[e];
-        }
-    for (int e = 0; e < d; ++e)
-        O[e] /= l;
-    *mx_out = mx;
-    *l_out = l;
-    *lse_out = mx + log(l);
-}
-
 /* Up to OR_SET query rows of one (host, batch, head) are evaluated in one
  * sweep over the keys, so each key/value row is read once per set instead of
  * once per query row.  Every row's arithmetic is exactly fwd_row's. */
@@ -324,6 +273,51 @@ int oracle_attn_rows(const float *Q, const float *K, const float *V, int n_hosts
     return 0;
 }
 
+/* Backward of a row set: after fwd_rowset, D = dO . O per row, then one more
+ * sweep over the keys accumulates dQ = scale * sum_k P (dO.v_k - D) k. */
+static void bwd_q_rowset(const or_dims *g, int nset, const double *const *dov,
+                         const long long *r, int qhost, int b, int kvh,
+                         double *const *sc, double *const *O, const double *lse,
+                         const double *D, double *const *dq)
+{
+    const int d = g->d;
+    const long long c = g->c;
+    long long tq[OR_SET];
+    double kd[512], vd[512];
+    for (int i = 0; i < nset; ++i) {
+        tq[i] = token_index(g->layout, g->n_hosts, c, qhost, r[i]);
+        for (int e = 0; e < d; ++e)
+            dq[i][e] = 0.0;
+    }
+    (void)O;
+    for (int j = 0; j < g->n_hosts; ++j)
+        for (long long rk = 0; rk < c; ++rk) {
+            long long tk = token_index(g->layout, g->n_hosts, c, j, rk);
+            int any = 0;
+            for (int i = 0; i < nset; ++i)
+                any |= visible(g->causal, tq[i], tk) && lse[i] != -INFINITY;
+            if (!any)
+                continue;
+            const float *k = K_ROW(g, j, b, kvh, rk);
+            const float *v = V_ROW(g, j, b, kvh, rk);
+            for (int e = 0; e < d; ++e) {
+                kd[e] = (double)k[e];
+                vd[e] = (double)v[e];
+            }
+            for (int i = 0; i < nset; ++i) {
+                if (!visible(g->causal, tq[i], tk) || lse[i] == -INFINITY)
+                    continue;
+                double p = exp(sc[i][j * c + rk] - lse[i]);
+                double dp = dot_d(vd, dov[i], d);
+                double ds = p * (dp - D[i]);
+                double *dqi = dq[i];
+#pragma omp simd
+                for (int e = 0; e < d; ++e)
+                    dqi[e] += g->scale * ds * kd[e];
+            }
+        }
+}
+
 /*
  * Backward for a list of query rows: dQ (n_rows x d), plus the row's LSE and
  * D = rowsum(dO * O) with O the oracle's own fp64 output.
@@ -336,59 +330,74 @@ int oracle_attn_bwd_q_rows(const float *Q, const float *K, const float *V,
                            const long long *rows, double *dQ, double *lse_out,
                            double *D_out)
 {
-    if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || d <= 0 || c <= 0 || n_hosts <= 0)
+    if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || d <= 0 || d > 512 || c <= 0 || n_hosts <= 0)
         return -1;
     or_dims g = {n_hosts, batch, hq, hkv, c, d, layout, causal, scale, K, V};
     const int group = hq / hkv;
-    int bad = 0;
-#pragma omp parallel for schedule(dynamic, 1)
     for (long long i = 0; i < n_rows; ++i) {
         const long long *rd = rows + 4 * i;
         int host = (int)rd[0], b = (int)rd[1], h = (int)rd[2];
         long long r = rd[3];
         if (host < 0 || host >= n_hosts || host < q_host_base ||
             host >= q_host_base + n_q_hosts || b < 0 || b >= batch || h < 0 || h >= hq ||
-            r < 0 || r >= c) {
-            bad = 1;
-            continue;
-        }
-        const int kvh = h / group;
-        double *q = (double *)malloc(sizeof(double) * ((size_t)d * 3 + (size_t)n_hosts * c));
-        double *o = q + d, *dov = q + 2 * d, *sc = q + 3 * d;
-        size_t qo = idx_row(&g, hq, host - q_host_base, b, h, r);
-        for (int e = 0; e < d; ++e) {
-            q[e] = (double)Q[qo + e];
-            dov[e] = (double)dO[qo + e];
-        }
-        double mxv, lv, lse;
-        fwd_row(&g, q, K, V, host, r, b, kvh, sc, o, &mxv, &lv, &lse);
-        double D = 0.0;
-        for (int e = 0; e < d; ++e)
-            D += dov[e] * o[e];
-        double *dq = dQ + (size_t)i * d;
-        for (int e = 0; e < d; ++e)
-            dq[e] = 0.0;
-        const long long tq = token_index(layout, n_hosts, c, host, r);
-        if (lse != -INFINITY) {
-            for (int j = 0; j < n_hosts; ++j)
-                for (long long rk = 0; rk < c; ++rk) {
-                    long long tk = token_index(layout, n_hosts, c, j, rk);
-                    if (!visible(causal, tq, tk))
-                        continue;
-                    size_t ko = idx_row(&g, hkv, j, b, kvh, rk);
-                    double p = exp(sc[(long long)j * c + rk] - lse);
-                    double dp = dot_f32(V + ko, dov, d);
-                    double ds = p * (dp - D);
-#pragma omp simd
-                    for (int e = 0; e < d; ++e)
-                        dq[e] += scale * ds * (double)K[ko + e];
-                }
-        }
-        lse_out[i] = lse;
-        D_out[i] = D;
-        free(q);
+            r < 0 || r >= c)
+            return -1;
     }
-    return bad ? -1 : 0;
+    long long *set_start = (long long *)malloc(sizeof(long long) * (size_t)(n_rows + 1));
+    long long n_sets = 0;
+    for (long long i = 0; i < n_rows;) {
+        long long j = i + 1;
+        while (j < n_rows && j - i < OR_SET && rows[4 * j] == rows[4 * i] &&
+               rows[4 * j + 1] == rows[4 * i + 1] && rows[4 * j + 2] == rows[4 * i + 2])
+            ++j;
+        set_start[n_sets++] = i;
+        i = j;
+    }
+    set_start[n_sets] = n_rows;
+#pragma omp parallel
+    {
+        double *buf = (double *)malloc(sizeof(double) * (size_t)OR_SET *
+                                       (3 * (size_t)d + (size_t)n_hosts * c + 2));
+#pragma omp for schedule(dynamic, 1)
+        for (long long s = 0; s < n_sets; ++s) {
+            const long long i0 = set_start[s];
+            const int nset = (int)(set_start[s + 1] - i0);
+            const long long *rd = rows + 4 * i0;
+            const int host = (int)rd[0], b = (int)rd[1], h = (int)rd[2];
+            double *qp[OR_SET], *op[OR_SET], *dop[OR_SET], *scp[OR_SET], *dqp[OR_SET];
+            double mx[OR_SET], lv[OR_SET], Dv[OR_SET];
+            long long rr[OR_SET];
+            double *area = buf + (size_t)OR_SET * 3 * d;
+            for (int i = 0; i < nset; ++i) {
+                qp[i] = buf + (size_t)i * 3 * d;
+                op[i] = qp[i] + d;
+                dop[i] = qp[i] + 2 * d;
+                scp[i] = area + (size_t)i * n_hosts * c;
+                dqp[i] = dQ + (size_t)(i0 + i) * d;
+                rr[i] = rows[4 * (i0 + i) + 3];
+                size_t qo = idx_row(&g, hq, host - q_host_base, b, h, rr[i]);
+                for (int e = 0; e < d; ++e) {
+                    qp[i][e] = (double)Q[qo + e];
+                    dop[i][e] = (double)dO[qo + e];
+                }
+            }
+            fwd_rowset(&g, nset, (const double *const *)qp, rr, host, b, h / group,
+                       (double *const *)scp, (double *const *)op, mx, lv, lse_out + i0);
+            for (int i = 0; i < nset; ++i) {
+                double acc = 0.0;
+                for (int e = 0; e < d; ++e)
+                    acc += dop[i][e] * op[i][e];
+                Dv[i] = acc;
+                D_out[i0 + i] = acc;
+            }
+            bwd_q_rowset(&g, nset, (const double *const *)dop, rr, host, b, h / group,
+                         (double *const *)scp, (double *const *)op, lse_out + i0, Dv,
+                         (double *const *)dqp);
+        }
+        free(buf);
+    }
+    free(set_start);
+    return 0;
 }
 
 /*
