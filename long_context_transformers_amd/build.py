@@ -16,7 +16,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
 def flags():
-    return ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    return ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fno-honor-nans",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
@@ -50,6 +50,12 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    # every kernel launched from host code must have its host stub in the library
+    und = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True).stdout
+    missing = [l for l in und.splitlines() if "__device_stub__" in l]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("libringattn.so would miss kernel stubs:\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     return LIB
 

@@ -107,7 +107,8 @@ void dkdv_kernel(BwdArgs a) {
   const int delta = a.delta[host];
   const int group = a.hq / a.hkv;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31,
+            hh = lane >> 5;
   const int k0 = kt * BK;
   const int kw0 = k0 + 32 * wave;             // this wave's first key
   const int key = kw0 + l32;                  // this lane's key (S columns)
@@ -361,7 +362,8 @@ void dq_kernel(BwdArgs a) {
   const int host = logical / a.batch;
   const int delta = a.delta[host];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31,
+            hh = lane >> 5;
   const int head = hg * HPW + wave / WPH;
   const int kvh = head / (a.hq / a.hkv);
   const int q0 = rt * ROWS;

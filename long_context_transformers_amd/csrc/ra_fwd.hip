@@ -34,7 +34,13 @@
 //  * Workgroup ids are remapped so that the 8 XCDs each take a contiguous
 //    range of (host, head) tiles (their K/V stay in that XCD's L2), and row
 //    tiles run heaviest first (causal blocks: later rows see more keys).
+#include <type_traits>
+
 #include "ra_internal.h"
+
+#ifndef RA_FWD_WAVES
+#define RA_FWD_WAVES 2   // waves per SIMD the forward kernel is built for
+#endif
 
 namespace ra {
 
@@ -55,40 +61,61 @@ __device__ inline int xcd_remap(int L, int T) {
 
 __device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-template <int D>
-struct FwdTile {
-  static constexpr int KS = D + 8;        // K row stride in LDS (bf16)
-  static constexpr int VS = kBN + 8;      // V^T row stride in LDS (bf16)
-  static constexpr int K_ELEMS = kBN * KS;
-  static constexpr int BUF = K_ELEMS + D * VS;
-  static constexpr int CPR = D / 8;       // 16-byte chunks per K row
-  static constexpr int K_LOADS = kBN * CPR / kThreads;           // per thread
-  static constexpr int V_BLOCKS = (kBN / 4) * (D / 8);           // 4 keys x 8 d micro-blocks
-  static constexpr int V_LOADS = (V_BLOCKS + kThreads - 1) / kThreads;
-  static_assert(kBN * CPR % kThreads == 0, "K tile split");
-};
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Position of 4-key group g (keys 4g..4g+3 of the tile) in the permuted V^T
-// row: within each 16-key chunk, bits 0 and 1 of the group index swap.
-__device__ inline int vt_group_pos(int g) {
-  return (g & ~3) | ((g & 1) << 1) | ((g >> 1) & 1);
+// Raw buffer resource over [p, p + nbytes): loads beyond nbytes return 0 (and
+// LDS-DMA loads beyond it write 0), so rows past the end of a block read as
+// zeros without branches.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, nbytes, 0x00020000);
+}
+__device__ inline uint4 bload16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// 16-byte LDS-DMA load: lane L's 16 bytes from r + voff land at lds + 16 L.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+
+// Lazy rescaling threshold (log2 units): the running reference max only moves
+// when a row's max grows by more than this, so P = 2^(s - m_ref) <= 2^8.
+constexpr float kRescaleThreshold = 8.0f;
+
+// K and V tiles of 64 keys live in LDS unpadded (rows of 2*D bytes) with the
+// 16-byte chunks of each row XOR-swizzled, filled by LDS-DMA buffer loads
+// (each lane's 16 bytes land at base + 16 * lane, so the swizzle is applied
+// by choosing which global chunk each lane fetches):
+//   K: LDS chunk C of row R holds global chunk C ^ (R % 8)  -> the score MFMA's
+//      A reads (rows 0..7 of a lane group, same chunk) hit distinct banks;
+//   V: LDS chunk C of row R holds global chunk C ^ 2 (R % 4) -> the transposing
+//      reads below (4 rows x 32 bytes per 16-lane group) hit distinct banks.
+template <int D>
+struct FwdTile {
+  static constexpr int ROWB = 2 * D;                 // bytes per row
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int TILE = kBN * ROWB;            // bytes per tile
+  static constexpr int DMA_PER_WAVE = kBN * CPR / 64 / 4;   // DMA instructions per wave per tile
+  static constexpr int BYTES = 4 * TILE;             // K[2], V[2]
+};
+
 template <int D, int HPW>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(RA_FWD_WAVES, RA_FWD_WAVES)))
 void fwd_bf16_kernel(FwdArgs a) {
   using T = FwdTile<D>;
   constexpr int WPH = 4 / HPW;          // waves per head
   constexpr int ROWS = 32 * WPH;        // query rows per workgroup
   constexpr int NDT = D / 32;           // 32-wide d tiles of O^T
   constexpr int NKK = D / 16;           // 16-deep steps of the score MFMA
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * T::BUF];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[T::BYTES];
 
   const int c = a.c;
   const int n_rt = (c + ROWS - 1) / ROWS;
   const int n_hg = a.hq / HPW;
-  const int total = gridDim.x;
-  int logical = xcd_remap(blockIdx.x, total);
+  int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int rt = n_rt - 1 - (logical % n_rt);
   logical /= n_rt;
   const int hg = logical % n_hg;
@@ -102,9 +129,12 @@ void fwd_bf16_kernel(FwdArgs a) {
   const int kend = min(c, row_last + delta + 1);   // keys [0, kend) can be visible
   if (kend <= 0) return;                           // nothing visible: state unchanged
   const int ntiles = (kend + kBN - 1) / kBN;
+  // leading tiles where every (row, key) pair of the workgroup is visible and in range
+  int n_unmasked = min((delta + q0 - (kBN - 1)) >= 0 ? (delta + q0 - (kBN - 1)) / kBN + 1 : 0, c / kBN);
+  n_unmasked = min(n_unmasked, ntiles);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;                        // lane half
@@ -114,12 +144,16 @@ void fwd_bf16_kernel(FwdArgs a) {
   const int qr = qw0 + l32;                        // this lane's query row
   const bool row_ok = qr < c;
 
+  const int blk_bytes = c * D * 2;
   const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + host * a.q_host_stride +
                      ((int64_t)(b * a.hq + head) * c) * D;
   const __bf16* kp = reinterpret_cast<const __bf16*>(a.k) + host * a.kv_host_stride +
                      ((int64_t)(b * a.hkv + kvh) * c) * D;
   const __bf16* vp = reinterpret_cast<const __bf16*>(a.v) + host * a.kv_host_stride +
                      ((int64_t)(b * a.hkv + kvh) * c) * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qp, blk_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp, blk_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp, blk_bytes);
   float* mp = a.m + host * a.ml_host_stride + (int64_t)(b * a.hq + head) * c;
   float* lp = a.l + host * a.ml_host_stride + (int64_t)(b * a.hq + head) * c;
   float* op = a.o + host * a.q_host_stride + ((int64_t)(b * a.hq + head) * c) * D;
@@ -127,22 +161,17 @@ void fwd_bf16_kernel(FwdArgs a) {
   // ---- Q fragments (B operand of S^T = K Q^T): d = 16kk + 8hh + j ----
   bf16x8 qf[NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row_ok) v = *reinterpret_cast<const uint4*>(qp + (int64_t)qr * D + 16 * kk + 8 * hh);
-    qf[kk] = as_bf16x8(v);
-  }
+  for (int kk = 0; kk < NKK; ++kk) qf[kk] = as_bf16x8(bload16(rq, (qr * D + 16 * kk + 8 * hh) * 2));
 
-  // ---- state: m (base 2 inside), per-half partial l, O^T accumulators ----
-  float m2 = -INFINITY, lh = 0.f;
+  // ---- state: reference max m_ref (base 2), true max, per-half partial l, O^T ----
+  float m_ref = -INFINITY, lh = 0.f;
   f32x16 acc_o[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[dt][r] = 0.f;
   if (row_ok) {
-    const float mn = mp[qr];
-    m2 = mn * kLog2e;                 // -inf stays -inf
+    m_ref = mp[qr] * kLog2e;          // -inf stays -inf
     lh = (hh == 0) ? lp[qr] : 0.f;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -155,161 +184,180 @@ void fwd_bf16_kernel(FwdArgs a) {
         acc_o[dt][4 * g + 3] = v.w;
       }
   }
+  float m_true = m_ref;
 
-  // ---- tile staging ----
-  uint4 rk[T::K_LOADS];
-  uint4 rv[T::V_LOADS][4];
-  auto load_tile = [&](int k0) {
+  // ---- LDS-DMA tile loads ----
+  // DMA instruction i of this wave fills LDS bytes [(wave*DPW + i) * 1024, +1024)
+  // of the tile: lane L writes LDS row R = idx / CPR, chunk C = idx % CPR with
+  // idx = (wave*DPW + i) * 64 + L, fetching global chunk C ^ swizzle(R).
+  // Row R = (wave*DPW + i) * RPI + lane / CPR (RPI = 64 / CPR rows per
+  // instruction, a multiple of 4), so R % 4 depends on the lane only and R % 8
+  // on the lane and the parity of wave*DPW + i.
+  constexpr int RPI = 64 / T::CPR;
+  const int lrow = lane / T::CPR, lch = lane % T::CPR;
+  const int lane_off = lrow * T::ROWB;
+  int kx[2];
 #pragma unroll
-    for (int i = 0; i < T::K_LOADS; ++i) {
-      const int qidx = tid + kThreads * i;
-      const int row = qidx / T::CPR, ch = qidx % T::CPR;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (k0 + row < c) v = *reinterpret_cast<const uint4*>(kp + (int64_t)(k0 + row) * D + 8 * ch);
-      rk[i] = v;
-    }
+  for (int p = 0; p < 2; ++p) kx[p] = (lch ^ ((RPI * p + lrow) & 7)) * 16;
+  const int vx = (lch ^ (2 * (lrow & 3))) * 16;
+  auto dma_k = [&](int t, int buf) {
+    unsigned char* base = smem + buf * T::TILE;
 #pragma unroll
-    for (int i = 0; i < T::V_LOADS; ++i) {
-      const int qidx = tid + kThreads * i;
-      const int g = qidx % 16, e = qidx / 16;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        const int key = k0 + 4 * g + kk;
-        if (qidx < T::V_BLOCKS && key < c)
-          v = *reinterpret_cast<const uint4*>(vp + (int64_t)key * D + 8 * e);
-        rv[i][kk] = v;
-      }
+    for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
+      const int ins = wave * T::DMA_PER_WAVE + i;
+      dma16(rk, base + ins * 1024, t * T::TILE + ins * RPI * T::ROWB + lane_off + kx[ins & 1]);
     }
   };
-  auto store_tile = [&](int buf) {
-    __bf16* ks = smem + buf * T::BUF;
-    __bf16* vs = ks + T::K_ELEMS;
+  auto dma_v = [&](int t, int buf) {
+    unsigned char* base = smem + (2 + buf) * T::TILE;
 #pragma unroll
-    for (int i = 0; i < T::K_LOADS; ++i) {
-      const int qidx = tid + kThreads * i;
-      const int row = qidx / T::CPR, ch = qidx % T::CPR;
-      *reinterpret_cast<uint4*>(ks + row * T::KS + 8 * ch) = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < T::V_LOADS; ++i) {
-      const int qidx = tid + kThreads * i;
-      if (qidx < T::V_BLOCKS) {
-        const int g = qidx % 16, e = qidx / 16;
-        const int col = 4 * vt_group_pos(g);
-        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&rv[i][0]);
-        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&rv[i][1]);
-        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&rv[i][2]);
-        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&rv[i][3]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int p = j >> 1;
-          uint2 o;
-          if ((j & 1) == 0) {
-            o.x = (w0[p] & 0xffffu) | (w1[p] << 16);
-            o.y = (w2[p] & 0xffffu) | (w3[p] << 16);
-          } else {
-            o.x = (w0[p] >> 16) | (w1[p] & 0xffff0000u);
-            o.y = (w2[p] >> 16) | (w3[p] & 0xffff0000u);
-          }
-          *reinterpret_cast<uint2*>(vs + (8 * e + j) * T::VS + col) = o;
-        }
-      }
+    for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
+      const int ins = wave * T::DMA_PER_WAVE + i;
+      dma16(rv, base + ins * 1024, t * T::TILE + ins * RPI * T::ROWB + lane_off + vx);
     }
   };
+  auto dma_wait = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
+  // ---- per-lane LDS read offsets ----
+  // scores: A operand row R = 32mt + l32, global chunk 2kk + hh, swizzle R % 8 = l32 % 8
+  const int ksw = l32 & 7;
+  // P V: transposing read r of K-step kk, d tile dt.  In each 16-lane group
+  // (G = lane / 16, j = lane % 16) lane j addresses row 16kk + 8r + 4h + j/4
+  // (h = G / 2) at columns 32dt + 16(G % 2) + 4(j % 4) .. +3; lane i of the
+  // group then receives column 32dt + 16(G % 2) + i of those four rows.
+  const int G = lane >> 4, jj = lane & 15;
+  const int va = jj & 3, vk = jj >> 2, vh = G >> 1, vdh = G & 1;
+  int v_off[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    const int row = 4 * vh + vk;                       // + 16kk + 8r (immediates)
+    const int chunk = 4 * dt + 2 * vdh + (va >> 1);
+    v_off[dt] = row * T::ROWB + ((chunk ^ (2 * vk)) * 16) + 8 * (va & 1);
+  }
+
+  auto scores = [&](int buf, f32x16 (&s)[2]) {
+    const unsigned char* ks = smem + buf * T::TILE;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int R = 32 * mt + l32;
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + R * T::ROWB + (((2 * kk + hh) ^ ksw) * 16));
+        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[mt], 0, 0, 0);
+      }
+  };
+  auto pv = [&](int buf, const bf16x8 (&pb)[4]) {
+    const unsigned char* vs = smem + (2 + buf) * T::TILE;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vs + v_off[dt] + (16 * kk) * T::ROWB));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vs + v_off[dt] + (16 * kk + 8) * T::ROWB));
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        const i16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb[kk], acc_o[dt], 0, 0, 0);
+      }
+  };
+  // masked row max of a score tile (base-2 units, combined over the two lane halves)
   const float c2 = a.scale_log2;
-  const bool wave_live = qw0 < c;
-
-  load_tile(0);
-  store_tile(0);
-  if (ntiles > 1) load_tile(kBN);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const int k0 = t * kBN;
-    const __bf16* ks = smem + buf * T::BUF;
-    const __bf16* vs = ks + T::K_ELEMS;
-    // wave-uniform classification of this tile against the band
-    const int dmin = k0 - (qw0 + 31);
-    const int dmax = k0 + kBN - 1 - qw0;
-    if (wave_live && visible(dmin, delta)) {
-      const bool need_mask = !visible(dmax, delta) || (k0 + kBN > c);
-      f32x16 s[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + (32 * mt + l32) * T::KS + 16 * kk + 8 * hh);
-          s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[mt], 0, 0, 0);
-        }
-      }
-      if (need_mask) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * mt + (r >> 2) * 8 + 4 * hh + (r & 3);
-            if (!(key < c && visible(key - qr, delta))) s[mt][r] = -INFINITY;
-          }
-      }
-      // row max over this tile (own 32 keys, then the other lane half)
-      float mx = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m2, mx * c2);
-      const bool dead = (m_new == -INFINITY);
-      const float alpha = dead ? 1.f : exp2f(m2 - m_new);
-      const float m_use = dead ? 0.f : m_new;
-      float rs = 0.f;
+  auto tile_max = [&](f32x16 (&s)[2], int k0, auto masked_tag) -> float {
+    if constexpr (decltype(masked_tag)::value) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][r], c2, -m_use));
-          s[mt][r] = p;
-          rs += p;
+          const int key = k0 + 32 * mt + (r >> 2) * 8 + 4 * hh + (r & 3);
+          if (!(key < c && visible(key - qr, delta))) s[mt][r] = -INFINITY;
         }
-      lh = lh * alpha + rs;
-      m2 = m_new;
+    }
+    float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[0][r], s[0][r + 1]));
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[1][r], s[1][r + 1]));
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c2;
+  };
+  // move the reference max (rescaling O and l) only when some row's max grew
+  // past the threshold
+  auto rescale = [&](float mx) {
+    m_true = fmaxf(m_true, mx);
+    if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_ref - m_new);
+      lh *= alpha;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
-      // P^T fragments: 16-key step kk uses values 8(kk%2)..+7 of key tile kk/2
-      bf16x8 pb[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pb[kk][j] = (__bf16)s[kk >> 1][8 * (kk & 1) + j];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(vs + (32 * dt + l32) * T::VS + 16 * kk + 8 * hh);
-          acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kk], acc_o[dt], 0, 0, 0);
-        }
+      m_ref = m_new;
     }
+  };
+  // P = 2^(S c2 - m_ref) as bf16 fragments: the 16-key step kk takes values
+  // 8(kk%2)..+7 of the 32-key half kk/2, i.e. keys 16kk + 8(j/4) + 4hh + j%4
+  auto exp_pack = [&](const f32x16 (&s)[2], bf16x8 (&pb)[4]) {
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+    float rs = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kk >> 1][8 * (kk & 1) + j], c2, -m_use));
+        rs += p;
+        pb[kk][j] = (__bf16)p;
+      }
+    lh += rs;
+  };
+
+  // ---- tile loop: iteration t computes and folds tile t; the DMA of tile
+  // t+1 into the other K/V buffers (last read in iteration t-1) overlaps it.
+  dma_k(0, 0);
+  dma_v(0, 0);
+  dma_wait();
+  __syncthreads();
+  auto step = [&](int t, auto masked) {
     if (t + 1 < ntiles) {
-      store_tile(buf ^ 1);
-      if (t + 2 < ntiles) load_tile(k0 + 2 * kBN);
+      dma_k(t + 1, (t + 1) & 1);
+      dma_v(t + 1, (t + 1) & 1);
     }
+    f32x16 s[2];
+    scores(t & 1, s);
+    const float mx = tile_max(s, t * kBN, masked);
+    rescale(mx);
+    bf16x8 pb[4];
+    exp_pack(s, pb);
+    pv(t & 1, pb);
+    // P V MFMAs with their transposing V reads running 2 MFMAs ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * NDT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    dma_wait();
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; ++t) {
+    if (t >= n_unmasked)
+      step(t, std::true_type{});
+    else
+      step(t, std::false_type{});
   }
 
-  // ---- write the state back ----
+  // ---- write the state back, referenced to the true running max ----
+  const float fix = (m_true == -INFINITY || m_ref == m_true) ? 1.f : exp2f(m_ref - m_true);
+  lh *= fix;
   const float l_tot = lh + __shfl_xor(lh, 32);
   if (row_ok) {
     if (hh == 0) {
-      mp[qr] = m2 * kLn2;
+      mp[qr] = m_true * kLn2;
       lp[qr] = l_tot;
     }
 #pragma unroll
@@ -317,10 +365,10 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         float4 v;
-        v.x = acc_o[dt][4 * g + 0];
-        v.y = acc_o[dt][4 * g + 1];
-        v.z = acc_o[dt][4 * g + 2];
-        v.w = acc_o[dt][4 * g + 3];
+        v.x = acc_o[dt][4 * g + 0] * fix;
+        v.y = acc_o[dt][4 * g + 1] * fix;
+        v.z = acc_o[dt][4 * g + 2] * fix;
+        v.w = acc_o[dt][4 * g + 3] * fix;
         *reinterpret_cast<float4*>(op + (int64_t)qr * D + 32 * dt + 8 * g + 4 * hh) = v;
       }
   }
@@ -357,7 +405,8 @@ void fwd_f32_kernel(FwdArgs a) {
   if (kend <= 0) return;
   const int ntiles = (kend + kBN - 1) / kBN;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31,
+            hh = lane >> 5;
   const int head = hg * HPW + wave / WPH;
   const int kvh = head / (a.hq / a.hkv);
   const int qw0 = q0 + (wave % WPH) * 32;

@@ -64,6 +64,9 @@ ra_status check_dims(const ra_dims* d) {
   if (!(d->scale >= 0.f) || std::isinf(d->scale))
     return fail(RA_ERR_INVALID_ARG, "scale must be finite and >= 0 (0 selects 1/sqrt(d))");
   if (d->block_len > (1 << 30)) return fail(RA_ERR_UNSUPPORTED, "block_len %d too large", d->block_len);
+  if ((int64_t)d->block_len * d->head_dim * 4 >= ((int64_t)1 << 31))
+    return fail(RA_ERR_UNSUPPORTED, "block of %d rows x %d too large (one head's block must stay below 2 GiB in fp32)",
+                d->block_len, d->head_dim);
   if ((int64_t)d->batch * d->heads_q > (1 << 24))
     return fail(RA_ERR_UNSUPPORTED, "batch * heads_q too large");
   return RA_OK;
