@@ -13,91 +13,126 @@
 // dQ += scale dS K, dK += scale dS^T Q.
 //
 // Two kernels per block, both deterministic (no floating-point atomics):
-//  * dkdv_kernel owns a tile of 128 keys (4 waves x 32) of one key/value head
-//    and sweeps every query tile (and every query head of the group) that can
-//    see it.  S = Q K^T is computed with keys on the MFMA's N side, so each
-//    lane owns one key; P and dS then sit in registers exactly as the A
-//    operand of dV += P^T dO and dK += dS^T Q needs them.  Q and dO tiles are
-//    staged in LDS both row-major (A operand of S and dP) and transposed with
-//    the key-style permutation (B operand of dV and dK).
-//  * dq_kernel owns query rows like the forward kernel (S^T orientation, one
-//    query per lane), recomputes P^T and dP^T = V dO^T per key tile and
-//    accumulates dQ^T += K^T dS^T; K is staged row-major and transposed, V
-//    row-major.
+//  * dkdv_kernel owns 128 keys (4 waves x 32) of one key/value head and
+//    sweeps every query tile (64 rows, every query head of the group) that
+//    can see them.  S = Q K^T and dP = dO V^T put one key per lane (keys on
+//    the MFMA's N side, K and V held in registers), so P and dS are directly
+//    the A operands of dV += P^T dO and dK += dS^T Q; the B operands dO^T and
+//    Q^T come from transposing LDS reads (ds_read_b64_tr_b16) of the same
+//    row-major tiles the score MFMAs read.
+//  * dq_kernel owns query rows like the forward kernel (one query per lane):
+//    S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T with K^T from transposing
+//    reads of the row-major K tile.
+// Q/dO (dkdv) and K/V (dq) tiles travel HBM -> LDS by LDS-DMA buffer loads,
+// double buffered, into an XOR swizzle that serves both access patterns:
+// LDS chunk C of row R holds global chunk C ^ (2 (R % 4) + (R / 4) % 2).
 // The dK/dV result is written as (partial sum received) + (this block's
 // contribution) to an output location that may belong to another host: the
 // ring driver uses that to hand the running sum to the neighbour.
+#include <type_traits>
+
 #include "ra_internal.h"
 
+#ifndef RA_DQ_WAVES
+#define RA_DQ_WAVES 2   // waves per SIMD the dQ kernel is built for
+#endif
+
 namespace ra {
+namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kBwdThreads = 256;
+constexpr int kTile = 64;                      // rows per staged tile
 constexpr float kBwdLog2e = 1.4426950408889634f;
 
-__device__ inline int bwd_xcd_remap(int L, int T) {
+__device__ inline int xcd_remap_b(int L, int T) {
   if (T % 8 != 0) return L;
   return (L % 8) * (T / 8) + (L / 8);
 }
-
-__device__ inline int perm_group_pos(int g) { return (g & ~3) | ((g & 1) << 1) | ((g >> 1) & 1); }
-
-__device__ inline bf16x8 to_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// Transposed, permuted store of a 4-row x 8-column bf16 micro-block held as
-// four 16-byte rows: rows 4g..4g+3 of the tile become columns at the permuted
-// position of group g in rows 8e..8e+7 of the transposed tile.
-__device__ inline void store_micro_t(__bf16* t, int ts, int g, int e, const uint4 (&w)[4]) {
-  const int col = 4 * perm_group_pos(g);
-  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&w[0]);
-  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&w[1]);
-  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&w[2]);
-  const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&w[3]);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int p = j >> 1;
-    uint2 o;
-    if ((j & 1) == 0) {
-      o.x = (w0[p] & 0xffffu) | (w1[p] << 16);
-      o.y = (w2[p] & 0xffffu) | (w3[p] << 16);
-    } else {
-      o.x = (w0[p] >> 16) | (w1[p] & 0xffff0000u);
-      o.y = (w2[p] >> 16) | (w3[p] & 0xffff0000u);
-    }
-    *reinterpret_cast<uint2*>(t + (8 * e + j) * ts + col) = o;
-  }
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* p, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, nbytes, 0x00020000);
 }
+__device__ inline uint4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ inline int swz(int R) { return 2 * (R & 3) + ((R >> 2) & 1); }
+
+// A tile of kTile rows x D bf16, row-major in LDS (2*D bytes per row, chunks
+// swizzled).  Wave `wave` fills its quarter with DMA: instruction i writes LDS
+// bytes [(wave*DPW + i) * 1024, +1024), lane L to row R = idx / CPR, chunk
+// C = idx % CPR (idx = (wave*DPW + i) * 64 + L), fetching global chunk C ^ swz(R).
+template <int D>
+struct STile {
+  static constexpr int ROWB = 2 * D;
+  static constexpr int CPR = D / 8;
+  static constexpr int BYTES = kTile * ROWB;
+  static constexpr int DPW = kTile * CPR / 64 / 4;
+  static constexpr int RPI = 64 / CPR;
+
+  __device__ static void dma(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int row0, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) {
+      const int ins = wave * DPW + i;
+      const int R = ins * RPI + lane / CPR;
+      const int C = lane % CPR;
+      dma16(r, lds + ins * 1024, (row0 + R) * ROWB + ((C ^ swz(R)) * 16));
+    }
+  }
+  // 16-byte row read: global chunk c of row R
+  __device__ static bf16x8 row(const unsigned char* lds, int R, int c) {
+    return *reinterpret_cast<const bf16x8*>(lds + R * ROWB + ((c ^ swz(R)) * 16));
+  }
+  // Transposed MFMA operand over 16 tile rows starting at rbase (a multiple of
+  // 16): lane (G = lane / 16, j = lane % 16) gets column dcol0 + 16 (G % 2) + j
+  // of rows rbase + 4 (G / 2) + 0..3 (items 0..3) and rbase + 8 + 4 (G / 2)
+  // + 0..3 (items 4..7).  In each 16-lane group of ds_read_b64_tr_b16, lane j
+  // addresses row rbase + 4 (G / 2) + j / 4 at columns dcol0 + 16 (G % 2)
+  // + 4 (j % 4) .. +3, and lane i receives column i of the four rows.
+  __device__ static bf16x8 tr(const unsigned char* lds, int rbase, int dcol0, int lane) {
+    const int G = lane >> 4, jj = lane & 15;
+    const int a = jj & 3, k = jj >> 2, h = G >> 1, dh = G & 1;
+    const int chunk = (dcol0 + 16 * dh + 4 * a) / 8;
+    const int s = 2 * k + h;                         // swz of rows rbase + 4h + k (+8)
+    const int off = (rbase + 4 * h + k) * ROWB + ((chunk ^ s) * 16) + 8 * (a & 1);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(lds + off));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(lds + off + 8 * ROWB));
+    const i16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, w);
+  }
+};
+
+__device__ inline void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+}  // namespace
 
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
 template <int D>
-struct KVTile {
-  static constexpr int BQ = 64;             // queries per tile
-  static constexpr int RS = D + 8;          // row-major stride (bf16)
-  static constexpr int TS = BQ + 8;         // transposed stride (bf16)
-  static constexpr int RM = BQ * RS;        // one row-major tile
-  static constexpr int TM = D * TS;         // one transposed tile
-  static constexpr int BUF = 2 * RM + 2 * TM + 2 * BQ * 2;   // Q, dO (both forms), lse2, D (floats as 2 bf16)
-  static constexpr int MB = (BQ / 4) * (D / 8);              // 4 x 8 micro-blocks per tile
-  static constexpr int MB_PER_T = (MB + kBwdThreads - 1) / kBwdThreads;
-};
-
-template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void dkdv_kernel(BwdArgs a) {
-  using T = KVTile<D>;
-  constexpr int BQ = T::BQ;
+  using T = STile<D>;
   constexpr int NKK = D / 16;
   constexpr int NDT = D / 32;
-  constexpr int BK = 128;                     // keys per workgroup
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * T::BUF];
+  constexpr int BK = 128;                                  // keys per workgroup
+  constexpr int BUF = 2 * T::BYTES + 2 * kTile * 4;        // Q, dO, lse2, D
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * BUF];
 
   const int c = a.c;
   const int n_kt = (c + BK - 1) / BK;
-  int logical = bwd_xcd_remap(blockIdx.x, gridDim.x);
+  int logical = xcd_remap_b(blockIdx.x, gridDim.x);
   const int kt = logical % n_kt;
   logical /= n_kt;
   const int kvh = logical % a.hkv;
@@ -107,28 +142,25 @@ void dkdv_kernel(BwdArgs a) {
   const int delta = a.delta[host];
   const int group = a.hq / a.hkv;
 
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31,
-            hh = lane >> 5;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int k0 = kt * BK;
-  const int kw0 = k0 + 32 * wave;             // this wave's first key
-  const int key = kw0 + l32;                  // this lane's key (S columns)
+  const int kw0 = k0 + 32 * wave;                          // this wave's first key
+  const int key = kw0 + l32;                               // this lane's key
   const bool key_ok = key < c;
+  const int blk_bytes = c * D * 2;
 
   const int64_t kvoff = host * a.kv_host_stride + ((int64_t)(b * a.hkv + kvh) * c) * D;
-  const __bf16* kp = reinterpret_cast<const __bf16*>(a.k) + kvoff;
-  const __bf16* vp = reinterpret_cast<const __bf16*>(a.v) + kvoff;
+  const __amdgpu_buffer_rsrc_t rk = rsrc(reinterpret_cast<const __bf16*>(a.k) + kvoff, blk_bytes);
+  const __amdgpu_buffer_rsrc_t rv = rsrc(reinterpret_cast<const __bf16*>(a.v) + kvoff, blk_bytes);
 
   // K^T and V^T fragments (B operands): lane = key, items = d 16kk + 8hh + j
   bf16x8 kf[NKK], vf[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
-    uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
-    if (key_ok) {
-      x = *reinterpret_cast<const uint4*>(kp + (int64_t)key * D + 16 * kk + 8 * hh);
-      y = *reinterpret_cast<const uint4*>(vp + (int64_t)key * D + 16 * kk + 8 * hh);
-    }
-    kf[kk] = to_bf16x8(x);
-    vf[kk] = to_bf16x8(y);
+    kf[kk] = as_bf16x8(bload16(rk, (key * D + 16 * kk + 8 * hh) * 2));
+    vf[kk] = as_bf16x8(bload16(rv, (key * D + 16 * kk + 8 * hh) * 2));
   }
   f32x16 acc_dk[NDT], acc_dv[NDT];
 #pragma unroll
@@ -141,99 +173,52 @@ void dkdv_kernel(BwdArgs a) {
 
   // queries that can see a key of this workgroup: q >= k0 - delta
   const int q_start = max(0, k0 - delta);
-  const int qt0 = q_start / BQ;
-  const int n_qt = (q_start >= c) ? 0 : (c + BQ - 1) / BQ - qt0;
-  const int n_iter = n_qt * group;            // (query head of the group, query tile)
+  const int qt0 = q_start / kTile;
+  const int n_qt = (q_start >= c) ? 0 : (c + kTile - 1) / kTile - qt0;
+  const int n_iter = n_qt * group;                         // (query head of the group, query tile)
 
-  // staging registers for one (head, query tile)
-  uint4 rq[T::MB_PER_T][4], ro[T::MB_PER_T][4];
-  float rl = 0.f, rd = 0.f;
-  auto load = [&](int it) {
+  float rl = INFINITY, rd = 0.f;                           // lse2 / D staging (threads < 64)
+  auto issue = [&](int it) {                               // DMA of Q, dO tile `it` + lse/D loads
     const int hg = it / n_qt;
-    const int q0 = (qt0 + it % n_qt) * BQ;
+    const int q0 = (qt0 + it % n_qt) * kTile;
     const int head = kvh * group + hg;
     const int64_t qoff = host * a.q_host_stride + ((int64_t)(b * a.hq + head) * c) * D;
-    const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + qoff;
-    const __bf16* op = reinterpret_cast<const __bf16*>(a.dO) + qoff;
-#pragma unroll
-    for (int i = 0; i < T::MB_PER_T; ++i) {
-      const int qidx = tid + kBwdThreads * i;
-      const int g = qidx % 16, e = qidx / 16;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int row = q0 + 4 * g + u;
-        uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
-        if (qidx < T::MB && row < c) {
-          x = *reinterpret_cast<const uint4*>(qp + (int64_t)row * D + 8 * e);
-          y = *reinterpret_cast<const uint4*>(op + (int64_t)row * D + 8 * e);
-        }
-        rq[i][u] = x;
-        ro[i][u] = y;
-      }
-    }
-    if (tid < BQ) {
+    const __amdgpu_buffer_rsrc_t rq = rsrc(reinterpret_cast<const __bf16*>(a.q) + qoff, blk_bytes);
+    const __amdgpu_buffer_rsrc_t ro = rsrc(reinterpret_cast<const __bf16*>(a.dO) + qoff, blk_bytes);
+    unsigned char* base = smem + (it & 1) * BUF;
+    T::dma(rq, base, q0, wave, lane);
+    T::dma(ro, base + T::BYTES, q0, wave, lane);
+    if (tid < kTile) {
       const int row = q0 + tid;
       const int64_t so = host * a.ml_host_stride + (int64_t)(b * a.hq + head) * c;
+      rl = INFINITY;
+      rd = 0.f;
       if (row < c) {
         const float lv = a.lse[so + row];
         rl = (lv == -INFINITY) ? INFINITY : lv * kBwdLog2e;   // rows without keys: P = 0
         rd = a.D[so + row];
-      } else {
-        rl = INFINITY;
-        rd = 0.f;
       }
     }
   };
-  auto store = [&](int buf) {
-    __bf16* base = smem + buf * T::BUF;
-    __bf16* q_rm = base;
-    __bf16* o_rm = base + T::RM;
-    __bf16* q_t = base + 2 * T::RM;
-    __bf16* o_t = q_t + T::TM;
-    float* lsep = reinterpret_cast<float*>(o_t + T::TM);
-    float* dp = lsep + BQ;
-#pragma unroll
-    for (int i = 0; i < T::MB_PER_T; ++i) {
-      const int qidx = tid + kBwdThreads * i;
-      if (qidx < T::MB) {
-        const int g = qidx % 16, e = qidx / 16;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          *reinterpret_cast<uint4*>(q_rm + (4 * g + u) * T::RS + 8 * e) = rq[i][u];
-          *reinterpret_cast<uint4*>(o_rm + (4 * g + u) * T::RS + 8 * e) = ro[i][u];
-        }
-        store_micro_t(q_t, T::TS, g, e, rq[i]);
-        store_micro_t(o_t, T::TS, g, e, ro[i]);
-      }
-    }
-    if (tid < BQ) {
-      lsep[tid] = rl;
-      dp[tid] = rd;
+  auto store_ld = [&](int it) {
+    if (tid < kTile) {
+      float* p = reinterpret_cast<float*>(smem + (it & 1) * BUF + 2 * T::BYTES);
+      p[tid] = rl;
+      p[kTile + tid] = rd;
     }
   };
 
   const float c2 = a.scale_log2;
-  if (n_iter > 0) {
-    load(0);
-    store(0);
-    if (n_iter > 1) load(1);
-  }
-  __syncthreads();
-  for (int it = 0; it < n_iter; ++it) {
-    const int buf = it & 1;
-    const int q0 = (qt0 + it % n_qt) * BQ;
-    const __bf16* base = smem + buf * T::BUF;
-    const __bf16* q_rm = base;
-    const __bf16* o_rm = base + T::RM;
-    const __bf16* q_t = base + 2 * T::RM;
-    const __bf16* o_t = q_t + T::TM;
-    const float* lsep = reinterpret_cast<const float*>(o_t + T::TM);
-    const float* dp = lsep + BQ;
-    // this wave's keys [kw0, kw0 + 32) against queries [q0, q0 + 64):
-    // visible iff key - query <= delta
-    const bool any = (kw0 < c) && visible(kw0 - (q0 + BQ - 1), delta);
-    if (any) {
-      const bool need_mask = !visible(kw0 + 31 - q0, delta) || (q0 + BQ > c) || (kw0 + 32 > c);
+  auto step = [&](int it, auto masked) {
+    if (it + 1 < n_iter) issue(it + 1);
+    const int q0 = (qt0 + it % n_qt) * kTile;
+    const unsigned char* base = smem + (it & 1) * BUF;
+    const unsigned char* qs = base;
+    const unsigned char* os = base + T::BYTES;
+    const float* lsep = reinterpret_cast<const float*>(base + 2 * T::BYTES);
+    const float* dp = lsep + kTile;
+    // keys [kw0, kw0+32) against queries [q0, q0+64): visible iff key - query <= delta
+    if ((kw0 < c) && visible(kw0 - (q0 + kTile - 1), delta)) {
       f32x16 s[2], dpv[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
@@ -246,10 +231,8 @@ void dkdv_kernel(BwdArgs a) {
       for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(q_rm + (32 * mt + l32) * T::RS + 16 * kk + 8 * hh);
-          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(o_rm + (32 * mt + l32) * T::RS + 16 * kk + 8 * hh);
-          s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s[mt], 0, 0, 0);
-          dpv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[kk], dpv[mt], 0, 0, 0);
+          s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::row(qs, 32 * mt + l32, 2 * kk + hh), kf[kk], s[mt], 0, 0, 0);
+          dpv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::row(os, 32 * mt + l32, 2 * kk + hh), vf[kk], dpv[mt], 0, 0, 0);
         }
       // P = exp2(S c2 - lse2), dS = P (dP - D); query of value r: 32mt + 8(r/4) + 4hh + r%4
 #pragma unroll
@@ -264,7 +247,7 @@ void dkdv_kernel(BwdArgs a) {
           for (int u = 0; u < 4; ++u) {
             const int r = 4 * g4 + u;
             float sv = s[mt][r];
-            if (need_mask) {
+            if constexpr (decltype(masked)::value) {
               const int qrow = q0 + 32 * mt + 8 * g4 + 4 * hh + u;
               if (!(key_ok && qrow < c && visible(key - qrow, delta))) sv = -INFINITY;
             }
@@ -285,17 +268,29 @@ void dkdv_kernel(BwdArgs a) {
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const bf16x8 ob = *reinterpret_cast<const bf16x8*>(o_t + (32 * dt + l32) * T::TS + 16 * kk + 8 * hh);
-          const bf16x8 qb = *reinterpret_cast<const bf16x8*>(q_t + (32 * dt + l32) * T::TS + 16 * kk + 8 * hh);
-          acc_dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], ob, acc_dv[dt], 0, 0, 0);
-          acc_dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsa[kk], qb, acc_dk[dt], 0, 0, 0);
+          acc_dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], T::tr(os, 16 * kk, 32 * dt, lane), acc_dv[dt], 0, 0, 0);
+          acc_dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsa[kk], T::tr(qs, 16 * kk, 32 * dt, lane), acc_dk[dt], 0, 0, 0);
         }
     }
-    if (it + 1 < n_iter) {
-      store(buf ^ 1);
-      if (it + 2 < n_iter) load(it + 2);
-    }
+    if (it + 1 < n_iter) store_ld(it + 1);
+    dma_wait();
     __syncthreads();
+  };
+
+  if (n_iter > 0) {
+    issue(0);
+    store_ld(0);
+    dma_wait();
+  }
+  __syncthreads();
+  for (int it = 0; it < n_iter; ++it) {
+    const int q0 = (qt0 + it % n_qt) * kTile;
+    // every pair of this workgroup visible and in range: no per-element mask
+    const bool full = visible(k0 + BK - 1 - q0, delta) && (q0 + kTile <= c) && (k0 + BK <= c);
+    if (full)
+      step(it, std::false_type{});
+    else
+      step(it, std::true_type{});
   }
 
   // epilogue: out = in + contribution (scale on dK); lane = d column, value r = key
@@ -327,33 +322,21 @@ void dkdv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-template <int D>
-struct QTile {
-  static constexpr int BK = 64;            // keys per tile
-  static constexpr int RS = D + 8;
-  static constexpr int TS = BK + 8;
-  static constexpr int RM = BK * RS;
-  static constexpr int TM = D * TS;
-  static constexpr int BUF = 2 * RM + TM;  // K row-major, V row-major, K transposed
-  static constexpr int MB = (BK / 4) * (D / 8);
-  static constexpr int MB_PER_T = (MB + kBwdThreads - 1) / kBwdThreads;
-};
-
 template <int D, int HPW>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(RA_DQ_WAVES, RA_DQ_WAVES)))
 void dq_kernel(BwdArgs a) {
-  using T = QTile<D>;
-  constexpr int BK = T::BK;
+  using T = STile<D>;
   constexpr int WPH = 4 / HPW;
   constexpr int ROWS = 32 * WPH;
   constexpr int NKK = D / 16;
   constexpr int NDT = D / 32;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * T::BUF];
+  constexpr int BUF = 2 * T::BYTES;                        // K, V
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * BUF];
 
   const int c = a.c;
   const int n_rt = (c + ROWS - 1) / ROWS;
   const int n_hg = a.hq / HPW;
-  int logical = bwd_xcd_remap(blockIdx.x, gridDim.x);
+  int logical = xcd_remap_b(blockIdx.x, gridDim.x);
   const int rt = n_rt - 1 - (logical % n_rt);
   logical /= n_rt;
   const int hg = logical % n_hg;
@@ -362,8 +345,9 @@ void dq_kernel(BwdArgs a) {
   const int host = logical / a.batch;
   const int delta = a.delta[host];
 
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31,
-            hh = lane >> 5;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int head = hg * HPW + wave / WPH;
   const int kvh = head / (a.hq / a.hkv);
   const int q0 = rt * ROWS;
@@ -372,28 +356,26 @@ void dq_kernel(BwdArgs a) {
   const bool row_ok = qr < c;
   const int row_last = min(q0 + ROWS, c) - 1;
   const int kend = min(c, row_last + delta + 1);
-  const int ntiles = kend > 0 ? (kend + BK - 1) / BK : 0;
-  if (ntiles == 0 && a.dq_accumulate) return;     // nothing visible: dQ unchanged
+  const int ntiles = kend > 0 ? (kend + kTile - 1) / kTile : 0;
+  if (ntiles == 0 && a.dq_accumulate) return;              // nothing visible: dQ unchanged
+  int n_unmasked = min((delta + q0 - (kTile - 1)) >= 0 ? (delta + q0 - (kTile - 1)) / kTile + 1 : 0, c / kTile);
+  n_unmasked = min(n_unmasked, ntiles);
+  const int blk_bytes = c * D * 2;
 
   const int64_t qoff = host * a.q_host_stride + ((int64_t)(b * a.hq + head) * c) * D;
-  const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + qoff;
-  const __bf16* op = reinterpret_cast<const __bf16*>(a.dO) + qoff;
+  const __amdgpu_buffer_rsrc_t rq = rsrc(reinterpret_cast<const __bf16*>(a.q) + qoff, blk_bytes);
+  const __amdgpu_buffer_rsrc_t ro = rsrc(reinterpret_cast<const __bf16*>(a.dO) + qoff, blk_bytes);
   const int64_t kvoff = host * a.kv_host_stride + ((int64_t)(b * a.hkv + kvh) * c) * D;
-  const __bf16* kp = reinterpret_cast<const __bf16*>(a.k) + kvoff;
-  const __bf16* vp = reinterpret_cast<const __bf16*>(a.v) + kvoff;
+  const __amdgpu_buffer_rsrc_t rk = rsrc(reinterpret_cast<const __bf16*>(a.k) + kvoff, blk_bytes);
+  const __amdgpu_buffer_rsrc_t rv = rsrc(reinterpret_cast<const __bf16*>(a.v) + kvoff, blk_bytes);
   const int64_t so = host * a.ml_host_stride + (int64_t)(b * a.hq + head) * c;
   float* dqp = a.dq + qoff;
 
   bf16x8 qf[NKK], of[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
-    uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
-    if (row_ok) {
-      x = *reinterpret_cast<const uint4*>(qp + (int64_t)qr * D + 16 * kk + 8 * hh);
-      y = *reinterpret_cast<const uint4*>(op + (int64_t)qr * D + 16 * kk + 8 * hh);
-    }
-    qf[kk] = to_bf16x8(x);
-    of[kk] = to_bf16x8(y);
+    qf[kk] = as_bf16x8(bload16(rq, (qr * D + 16 * kk + 8 * hh) * 2));
+    of[kk] = as_bf16x8(bload16(ro, (qr * D + 16 * kk + 8 * hh) * 2));
   }
   float lse2 = INFINITY, Dq = 0.f;
   if (row_ok) {
@@ -407,107 +389,68 @@ void dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
 
-  uint4 rkm[T::MB_PER_T][4], rv[T::MB_PER_T][4];
-  auto load = [&](int kb0) {
-#pragma unroll
-    for (int i = 0; i < T::MB_PER_T; ++i) {
-      const int qidx = tid + kBwdThreads * i;
-      const int g = qidx % 16, e = qidx / 16;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int row = kb0 + 4 * g + u;
-        uint4 x = make_uint4(0, 0, 0, 0), y = make_uint4(0, 0, 0, 0);
-        if (qidx < T::MB && row < c) {
-          x = *reinterpret_cast<const uint4*>(kp + (int64_t)row * D + 8 * e);
-          y = *reinterpret_cast<const uint4*>(vp + (int64_t)row * D + 8 * e);
-        }
-        rkm[i][u] = x;
-        rv[i][u] = y;
-      }
+  const float c2 = a.scale_log2;
+  auto step = [&](int t, auto masked) {
+    if (t + 1 < ntiles) {
+      unsigned char* nb = smem + ((t + 1) & 1) * BUF;
+      T::dma(rk, nb, (t + 1) * kTile, wave, lane);
+      T::dma(rv, nb + T::BYTES, (t + 1) * kTile, wave, lane);
     }
-  };
-  auto store = [&](int buf) {
-    __bf16* k_rm = smem + buf * T::BUF;
-    __bf16* v_rm = k_rm + T::RM;
-    __bf16* k_t = v_rm + T::RM;
+    const int kb0 = t * kTile;
+    const unsigned char* ks = smem + (t & 1) * BUF;
+    const unsigned char* vs = ks + T::BYTES;
+    f32x16 s[2], dpv[2];
 #pragma unroll
-    for (int i = 0; i < T::MB_PER_T; ++i) {
-      const int qidx = tid + kBwdThreads * i;
-      if (qidx < T::MB) {
-        const int g = qidx % 16, e = qidx / 16;
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          *reinterpret_cast<uint4*>(k_rm + (4 * g + u) * T::RS + 8 * e) = rkm[i][u];
-          *reinterpret_cast<uint4*>(v_rm + (4 * g + u) * T::RS + 8 * e) = rv[i][u];
-        }
-        store_micro_t(k_t, T::TS, g, e, rkm[i]);
+      for (int r = 0; r < 16; ++r) {
+        s[mt][r] = 0.f;
+        dpv[mt][r] = 0.f;
       }
-    }
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::row(ks, 32 * mt + l32, 2 * kk + hh), qf[kk], s[mt], 0, 0, 0);
+        dpv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::row(vs, 32 * mt + l32, 2 * kk + hh), of[kk], dpv[mt], 0, 0, 0);
+      }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float sv = s[mt][r];
+        if constexpr (decltype(masked)::value) {
+          const int kr = kb0 + 32 * mt + (r >> 2) * 8 + 4 * hh + (r & 3);
+          if (!(kr < c && visible(kr - qr, delta))) sv = -INFINITY;
+        }
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c2, -lse2));
+        dpv[mt][r] = p * (dpv[mt][r] - Dq);
+      }
+    bf16x8 dsb[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dsb[kk][j] = (__bf16)dpv[kk >> 1][8 * (kk & 1) + j];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::tr(ks, 16 * kk, 32 * dt, lane), dsb[kk], acc[dt], 0, 0, 0);
+    dma_wait();
+    __syncthreads();
   };
 
-  const float c2 = a.scale_log2;
-  const bool wave_live = qw0 < c;
   if (ntiles > 0) {
-    load(0);
-    store(0);
-    if (ntiles > 1) load(BK);
+    T::dma(rk, smem, 0, wave, lane);
+    T::dma(rv, smem + T::BYTES, 0, wave, lane);
+    dma_wait();
   }
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const int kb0 = t * BK;
-    const __bf16* k_rm = smem + buf * T::BUF;
-    const __bf16* v_rm = k_rm + T::RM;
-    const __bf16* k_t = v_rm + T::RM;
-    if (wave_live && visible(kb0 - (qw0 + 31), delta)) {
-      const bool need_mask = !visible(kb0 + BK - 1 - qw0, delta) || (kb0 + BK > c);
-      f32x16 s[2], dpv[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[mt][r] = 0.f;
-          dpv[mt][r] = 0.f;
-        }
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(k_rm + (32 * mt + l32) * T::RS + 16 * kk + 8 * hh);
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(v_rm + (32 * mt + l32) * T::RS + 16 * kk + 8 * hh);
-          s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[mt], 0, 0, 0);
-          dpv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, of[kk], dpv[mt], 0, 0, 0);
-        }
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float sv = s[mt][r];
-          if (need_mask) {
-            const int kr = kb0 + 32 * mt + (r >> 2) * 8 + 4 * hh + (r & 3);
-            if (!(kr < c && visible(kr - qr, delta))) sv = -INFINITY;
-          }
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c2, -lse2));
-          dpv[mt][r] = p * (dpv[mt][r] - Dq);
-        }
-      bf16x8 dsb[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dsb[kk][j] = (__bf16)dpv[kk >> 1][8 * (kk & 1) + j];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const bf16x8 kta = *reinterpret_cast<const bf16x8*>(k_t + (32 * dt + l32) * T::TS + 16 * kk + 8 * hh);
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kta, dsb[kk], acc[dt], 0, 0, 0);
-        }
-    }
-    if (t + 1 < ntiles) {
-      store(buf ^ 1);
-      if (t + 2 < ntiles) load(kb0 + 2 * BK);
-    }
-    __syncthreads();
+    if (t >= n_unmasked)
+      step(t, std::true_type{});
+    else
+      step(t, std::false_type{});
   }
 
   if (row_ok) {
