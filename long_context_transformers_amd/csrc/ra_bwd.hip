@@ -179,8 +179,8 @@ void dkdv_kernel(BwdArgs a) {
 
   float rl = INFINITY, rd = 0.f;                           // lse2 / D staging (threads < 64)
   auto issue = [&](int it) {                               // DMA of Q, dO tile `it` + lse/D loads
-    const int hg = it / n_qt;
-    const int q0 = (qt0 + it % n_qt) * kTile;
+    const int hg = it % group;
+    const int q0 = (qt0 + it / group) * kTile;
     const int head = kvh * group + hg;
     const int64_t qoff = host * a.q_host_stride + ((int64_t)(b * a.hq + head) * c) * D;
     const __amdgpu_buffer_rsrc_t rq = rsrc(reinterpret_cast<const __bf16*>(a.q) + qoff, blk_bytes);
@@ -211,7 +211,7 @@ void dkdv_kernel(BwdArgs a) {
   const float c2 = a.scale_log2;
   auto step = [&](int it, auto masked) {
     if (it + 1 < n_iter) issue(it + 1);
-    const int q0 = (qt0 + it % n_qt) * kTile;
+    const int q0 = (qt0 + it / group) * kTile;
     const unsigned char* base = smem + (it & 1) * BUF;
     const unsigned char* qs = base;
     const unsigned char* os = base + T::BYTES;
@@ -283,15 +283,21 @@ void dkdv_kernel(BwdArgs a) {
     dma_wait();
   }
   __syncthreads();
-  for (int it = 0; it < n_iter; ++it) {
-    const int q0 = (qt0 + it % n_qt) * kTile;
-    // every pair of this workgroup visible and in range: no per-element mask
-    const bool full = visible(k0 + BK - 1 - q0, delta) && (q0 + kTile <= c) && (k0 + BK <= c);
-    if (full)
-      step(it, std::false_type{});
-    else
-      step(it, std::true_type{});
+  // Query tiles run in order (heads of the group innermost); tile qt needs no
+  // per-element mask when every pair of this workgroup is visible and in
+  // range: qt >= qt_full (diagonal band above) and a complete tile.  Masked
+  // head, unmasked middle and masked tail run as separate loops so the
+  // accumulators keep their registers across iterations.
+  int it_a = n_iter, it_b = n_iter;
+  if (k0 + BK <= c) {
+    const int need = k0 + BK - 1 - delta;                   // smallest fully visible q0
+    const int qt_full = need <= 0 ? 0 : (need + kTile - 1) / kTile;
+    it_a = min(n_iter, max(0, qt_full - qt0) * group);
+    it_b = max(it_a, n_iter - ((c % kTile) ? group : 0));
   }
+  for (int it = 0; it < it_a; ++it) step(it, std::true_type{});
+  for (int it = it_a; it < it_b; ++it) step(it, std::false_type{});
+  for (int it = it_b; it < n_iter; ++it) step(it, std::true_type{});
 
   // epilogue: out = in + contribution (scale on dK); lane = d column, value r = key
   const int out_host = (host + a.dkv_out_host_shift) % a.n_hosts;
@@ -446,12 +452,8 @@ void dq_kernel(BwdArgs a) {
     dma_wait();
   }
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    if (t >= n_unmasked)
-      step(t, std::true_type{});
-    else
-      step(t, std::false_type{});
-  }
+  for (int t = 0; t < n_unmasked; ++t) step(t, std::false_type{});
+  for (int t = n_unmasked; t < ntiles; ++t) step(t, std::true_type{});
 
   if (row_ok) {
     const float scale = a.scale;

@@ -344,12 +344,8 @@ void fwd_bf16_kernel(FwdArgs a) {
     dma_wait();
     __syncthreads();
   };
-  for (int t = 0; t < ntiles; ++t) {
-    if (t >= n_unmasked)
-      step(t, std::true_type{});
-    else
-      step(t, std::false_type{});
-  }
+  for (int t = 0; t < n_unmasked; ++t) step(t, std::false_type{});
+  for (int t = n_unmasked; t < ntiles; ++t) step(t, std::true_type{});
 
   // ---- write the state back, referenced to the true running max ----
   const float fix = (m_true == -INFINITY || m_ref == m_true) ? 1.f : exp2f(m_ref - m_true);
