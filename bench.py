@@ -249,6 +249,30 @@ def elementwise_bw(torch, ra, reps=10):
             "peak_GBs": PEAK_HBM_GBS}
 
 
+def reference_gemm(torch, n=8192, reps=20):
+    """This GPU's bf16 GEMM rate (torch.matmul, n^3, N(0,1) operands): a
+    measured ceiling for dense bf16 contractions on random data, beside the
+    published peak (matrix-core throughput on this part drops with random
+    operand data, so the published peak is not reachable by real inputs)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    a = torch.randn((n, n), device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn((n, n), device="cuda", dtype=torch.bfloat16, generator=g)
+    for _ in range(3):
+        c = a @ b
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ b
+    e1.record()
+    e1.synchronize()
+    del c
+    ms = e0.elapsed_time(e1) / reps
+    return {"tflops": 2.0 * n ** 3 / (ms / 1e3) / 1e12, "shape": [n, n, n], "operands": "randn bf16",
+            "ms": ms}
+
+
 def causal_rates(torch, ra, steps=3):
     """Forward TFLOP/s of the causal 256K host-7 workload in both layouts and
     of the 786K striped GQA host-15 workload (seeded device-side inputs)."""
@@ -344,6 +368,10 @@ def main():
         extra["overlap"] = tcalc_sweep(torch, ra)
         log("[bench] finalize / merge bandwidth")
         extra["elementwise"] = elementwise_bw(torch, ra)
+        log("[bench] reference bf16 GEMM")
+        extra["reference_gemm"] = reference_gemm(torch)
+        extra["dominant_kernel_vs_reference_gemm"] = achieved / extra["reference_gemm"]["tflops"]
+        extra["fwd_kernel_vs_reference_gemm"] = extra["fwd_kernel_tflops"] / extra["reference_gemm"]["tflops"]
 
     cpu = None
     if not args.no_cpu_baseline:

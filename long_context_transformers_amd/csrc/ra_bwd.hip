@@ -24,96 +24,45 @@
 //    S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T with K^T from transposing
 //    reads of the row-major K tile.
 // Q/dO (dkdv) and K/V (dq) tiles travel HBM -> LDS by LDS-DMA buffer loads,
-// double buffered, into an XOR swizzle that serves both access patterns:
-// LDS chunk C of row R holds global chunk C ^ (2 (R % 4) + (R / 4) % 2).
+// double buffered, into the swizzled row-major layout of ra_tile.h, which
+// serves both the row reads and the transposing reads without bank conflicts.
 // The dK/dV result is written as (partial sum received) + (this block's
 // contribution) to an output location that may belong to another host: the
 // ring driver uses that to hand the running sum to the neighbour.
 #include <type_traits>
 
 #include "ra_internal.h"
+#include "ra_tile.h"
 
 #ifndef RA_DQ_WAVES
 #define RA_DQ_WAVES 2   // waves per SIMD the dQ kernel is built for
+#endif
+#ifndef RA_DKDV_STAGES
+#define RA_DKDV_STAGES 4   // LDS stages of the dK/dV kernel's query-tile pipeline (3 or 4)
+#endif
+#ifndef RA_DKDV_PREFETCH
+#define RA_DKDV_PREFETCH 3   // MFMAs by which the dK/dV kernel's LDS operand reads run ahead
 #endif
 
 namespace ra {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void lds_void;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+using tile::as_bf16x8;
+using tile::bf16x8;
+using tile::bload16;
+using tile::dma_wait;
+using tile::rsrc;
 
 constexpr int kBwdThreads = 256;
-constexpr int kTile = 64;                      // rows per staged tile
+constexpr int kTile = tile::kRows;             // rows per staged tile
 constexpr float kBwdLog2e = 1.4426950408889634f;
 
 __device__ inline int xcd_remap_b(int L, int T) {
   if (T % 8 != 0) return L;
   return (L % 8) * (T / 8) + (L / 8);
 }
-__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* p, int nbytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, nbytes, 0x00020000);
-}
-__device__ inline uint4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-__device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
-}
-__device__ inline int swz(int R) { return 2 * (R & 3) + ((R >> 2) & 1); }
-
-// A tile of kTile rows x D bf16, row-major in LDS (2*D bytes per row, chunks
-// swizzled).  Wave `wave` fills its quarter with DMA: instruction i writes LDS
-// bytes [(wave*DPW + i) * 1024, +1024), lane L to row R = idx / CPR, chunk
-// C = idx % CPR (idx = (wave*DPW + i) * 64 + L), fetching global chunk C ^ swz(R).
-template <int D>
-struct STile {
-  static constexpr int ROWB = 2 * D;
-  static constexpr int CPR = D / 8;
-  static constexpr int BYTES = kTile * ROWB;
-  static constexpr int DPW = kTile * CPR / 64 / 4;
-  static constexpr int RPI = 64 / CPR;
-
-  __device__ static void dma(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int row0, int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < DPW; ++i) {
-      const int ins = wave * DPW + i;
-      const int R = ins * RPI + lane / CPR;
-      const int C = lane % CPR;
-      dma16(r, lds + ins * 1024, (row0 + R) * ROWB + ((C ^ swz(R)) * 16));
-    }
-  }
-  // 16-byte row read: global chunk c of row R
-  __device__ static bf16x8 row(const unsigned char* lds, int R, int c) {
-    return *reinterpret_cast<const bf16x8*>(lds + R * ROWB + ((c ^ swz(R)) * 16));
-  }
-  // Transposed MFMA operand over 16 tile rows starting at rbase (a multiple of
-  // 16): lane (G = lane / 16, j = lane % 16) gets column dcol0 + 16 (G % 2) + j
-  // of rows rbase + 4 (G / 2) + 0..3 (items 0..3) and rbase + 8 + 4 (G / 2)
-  // + 0..3 (items 4..7).  In each 16-lane group of ds_read_b64_tr_b16, lane j
-  // addresses row rbase + 4 (G / 2) + j / 4 at columns dcol0 + 16 (G % 2)
-  // + 4 (j % 4) .. +3, and lane i receives column i of the four rows.
-  __device__ static bf16x8 tr(const unsigned char* lds, int rbase, int dcol0, int lane) {
-    const int G = lane >> 4, jj = lane & 15;
-    const int a = jj & 3, k = jj >> 2, h = G >> 1, dh = G & 1;
-    const int chunk = (dcol0 + 16 * dh + 4 * a) / 8;
-    const int s = 2 * k + h;                         // swz of rows rbase + 4h + k (+8)
-    const int off = (rbase + 4 * h + k) * ROWB + ((chunk ^ s) * 16) + 8 * (a & 1);
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(lds + off));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(lds + off + 8 * ROWB));
-    const i16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, w);
-  }
-};
-
-__device__ inline void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 }  // namespace
 
@@ -123,12 +72,15 @@ __device__ inline void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memor
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void dkdv_kernel(BwdArgs a) {
-  using T = STile<D>;
+  using T = tile::STile<D>;
   constexpr int NKK = D / 16;
   constexpr int NDT = D / 32;
   constexpr int BK = 128;                                  // keys per workgroup
-  constexpr int BUF = 2 * T::BYTES + 2 * kTile * 4;        // Q, dO, lse2, D
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * BUF];
+  constexpr int BUF = 2 * T::BYTES + 2 * kTile * 4;        // Q, dO, lse, D of one query tile
+  constexpr int NS = RA_DKDV_STAGES;                       // LDS stages (tiles in flight + 1)
+  constexpr int NV = 2 * T::DPW + 1;                       // DMA instructions per wave per tile
+  static_assert(NS >= 2 && NS <= 4, "wait_tile handles up to two newer tiles");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * BUF];
 
   const int c = a.c;
   const int n_kt = (c + BK - 1) / BK;
@@ -177,111 +129,168 @@ void dkdv_kernel(BwdArgs a) {
   const int n_qt = (q_start >= c) ? 0 : (c + kTile - 1) / kTile - qt0;
   const int n_iter = n_qt * group;                         // (query head of the group, query tile)
 
-  float rl = INFINITY, rd = 0.f;                           // lse2 / D staging (threads < 64)
-  auto issue = [&](int it) {                               // DMA of Q, dO tile `it` + lse/D loads
+  // Tile `it` (query tile qt0 + it / group of query head kvh*group + it % group)
+  // goes to stage it % NS by LDS-DMA: Q and dO rows, and the 64 lse and D
+  // values (32 per wave: lse rows 0..31, 32..63 from waves 0, 1; D from
+  // waves 2, 3; lanes 0..7).  Rows past the block read as 0.
+  auto issue = [&](int it) {
     const int hg = it % group;
     const int q0 = (qt0 + it / group) * kTile;
     const int head = kvh * group + hg;
     const int64_t qoff = host * a.q_host_stride + ((int64_t)(b * a.hq + head) * c) * D;
     const __amdgpu_buffer_rsrc_t rq = rsrc(reinterpret_cast<const __bf16*>(a.q) + qoff, blk_bytes);
     const __amdgpu_buffer_rsrc_t ro = rsrc(reinterpret_cast<const __bf16*>(a.dO) + qoff, blk_bytes);
-    unsigned char* base = smem + (it & 1) * BUF;
+    unsigned char* base = smem + (it % NS) * BUF;
     T::dma(rq, base, q0, wave, lane);
     T::dma(ro, base + T::BYTES, q0, wave, lane);
-    if (tid < kTile) {
-      const int row = q0 + tid;
-      const int64_t so = host * a.ml_host_stride + (int64_t)(b * a.hq + head) * c;
-      rl = INFINITY;
-      rd = 0.f;
-      if (row < c) {
-        const float lv = a.lse[so + row];
-        rl = (lv == -INFINITY) ? INFINITY : lv * kBwdLog2e;   // rows without keys: P = 0
-        rd = a.D[so + row];
-      }
-    }
+    const int64_t so = host * a.ml_host_stride + (int64_t)(b * a.hq + head) * c;
+    const __amdgpu_buffer_rsrc_t rs = rsrc((wave < 2 ? a.lse : a.D) + so, c * 4);
+    if (lane < 8) tile::dma16(rs, base + 2 * T::BYTES + wave * 128, (q0 + 32 * (wave & 1)) * 4 + 16 * lane);
   };
-  auto store_ld = [&](int it) {
-    if (tid < kTile) {
-      float* p = reinterpret_cast<float*>(smem + (it & 1) * BUF + 2 * T::BYTES);
-      p[tid] = rl;
-      p[kTile + tid] = rd;
-    }
+  // Wait until tile `need` has landed, given that tiles up to `last` were
+  // issued (VMEM completes in issue order; each tile is NV instructions).
+  auto wait_tile = [&](int need, int last) {
+    const int newer = min(NS - 2, last - need);
+    if (NS >= 4 && newer >= 2) tile::vm_wait<2 * NV>();
+    else if (newer >= 1) tile::vm_wait<NV>();
+    else tile::vm_wait<0>();
+  };
+
+  // Loop-invariant LDS offsets.  Row reads: row R = 32mt + l32 (the swizzle
+  // depends on R mod 16 only), global chunk 2kk + hh.  Transposing reads: the
+  // two halves of the operand for d tile dt at rows 16kk.. .
+  int roff[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) roff[kk] = l32 * T::ROWB + (((2 * kk + hh) ^ tile::swz<D>(l32)) * 16);
+  int tlo[NDT], thi[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    tlo[dt] = T::tr_off(0, 32 * dt, lane);
+    thi[dt] = T::tr_off(8, 32 * dt, lane);
+  }
+  auto rowa = [&](const unsigned char* t, int mt, int kk) {
+    return *reinterpret_cast<const bf16x8*>(t + 32 * mt * T::ROWB + roff[kk]);
   };
 
   const float c2 = a.scale_log2;
-  auto step = [&](int it, auto masked) {
-    if (it + 1 < n_iter) issue(it + 1);
+  // One query tile against this wave's 32 keys.  Phases, in issue order:
+  //  A  S = Q K^T and dP = dO V^T, query half mt = 0 then mt = 1 (S and dP
+  //     chains alternate, so consecutive MFMAs are independent);
+  //  B  P = 2^(S c2 - lse2), dS = P (dP - D) for half 0 while the MFMAs of
+  //     half 1 run, then for half 1 while the first dV/dK MFMAs run;
+  //  C  dV += P^T dO, dK += dS^T Q (transposing reads of the same tiles).
+  // LDS reads are kept two to three MFMAs ahead of their use.
+  auto compute = [&](int it, auto masked) {
     const int q0 = (qt0 + it / group) * kTile;
-    const unsigned char* base = smem + (it & 1) * BUF;
+    const unsigned char* base = smem + (it % NS) * BUF;
     const unsigned char* qs = base;
     const unsigned char* os = base + T::BYTES;
     const float* lsep = reinterpret_cast<const float*>(base + 2 * T::BYTES);
     const float* dp = lsep + kTile;
-    // keys [kw0, kw0+32) against queries [q0, q0+64): visible iff key - query <= delta
-    if ((kw0 < c) && visible(kw0 - (q0 + kTile - 1), delta)) {
-      f32x16 s[2], dpv[2];
+    f32x16 s[2], dpv[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s[mt][r] = 0.f;
-          dpv[mt][r] = 0.f;
+      for (int r = 0; r < 16; ++r) {
+        s[mt][r] = 0.f;
+        dpv[mt][r] = 0.f;
+      }
+    // A: MFMA j of 4 NKK: half mt = j / (2 NKK), d step kk = (j / 2) % NKK,
+    // S (j even) or dP (j odd); operands read kPre MFMAs ahead.
+    constexpr int NA = 4 * NKK, kPre = RA_DKDV_PREFETCH;
+    auto a_read = [&](int j) {
+      return rowa((j & 1) ? os : qs, j / (2 * NKK), (j / 2) % NKK);
+    };
+    // C: MFMA j of 8 NDT: kk = j / (2 NDT), dt = (j / 2) % NDT, dV (j even)
+    // or dK (j odd); transposing operand reads kPre MFMAs ahead.
+    constexpr int NC = 8 * NDT;
+    auto c_read = [&](int j) {
+      const int kk = j / (2 * NDT), dt = (j / 2) % NDT;
+      return T::tr_at(((j & 1) ? qs : os) + 16 * kk * T::ROWB, tlo[dt], thi[dt]);
+    };
+    // B, one element at a time: value r of half mt belongs to query
+    // 32mt + 8(r/4) + 4hh + r%4 and lands in item r%8 of pa/dsa[2mt + r/8].
+    float la[2][16], da[2][16];
+    auto ld_read = [&](int mt) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        // one typed vector load each (keeps the load's alias information, see ra_tile.h)
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(lsep + 32 * mt + 8 * g4 + 4 * hh);
+        const f32x4 dv = *reinterpret_cast<const f32x4*>(dp + 32 * mt + 8 * g4 + 4 * hh);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          la[mt][4 * g4 + u] = lv[u] * kBwdLog2e;   // lse in base 2
+          da[mt][4 * g4 + u] = dv[u];
         }
+      }
+    };
+    bf16x8 pa[4], dsa[4];
+    // (every row of an unmasked tile sees a key, so its lse is finite; in a
+    // masked tile, invisible pairs, which include every pair of a row that
+    // sees no key at all, get P = 0 by selection)
+    auto softmax_elem = [&](int mt, int r) {
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][r], c2, -la[mt][r]));
+      if constexpr (decltype(masked)::value) {
+        const int qrow = q0 + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (!(key_ok && qrow < c && visible(key - qrow, delta))) p = 0.f;
+      }
+      pa[2 * mt + (r >> 3)][r & 7] = (__bf16)p;
+      dsa[2 * mt + (r >> 3)][r & 7] = (__bf16)(p * (dpv[mt][r] - da[mt][r]));
+    };
+
+    constexpr int EA = 16 / (NA / 2), EC = 16 / (NC / 2);   // softmax values per MFMA slot
+    static_assert(EA * (NA / 2) == 16 && EC * (NC / 2) == 16, "slots must divide a half's 16 values");
+    bf16x8 aop[NA], cop[NC];
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
+    for (int j = 0; j < kPre; ++j) aop[j] = a_read(j);
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::row(qs, 32 * mt + l32, 2 * kk + hh), kf[kk], s[mt], 0, 0, 0);
-          dpv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::row(os, 32 * mt + l32, 2 * kk + hh), vf[kk], dpv[mt], 0, 0, 0);
-        }
-      // P = exp2(S c2 - lse2), dS = P (dP - D); query of value r: 32mt + 8(r/4) + 4hh + r%4
+    for (int j = 0; j < NA; ++j) {
+      if (j + kPre < NA) aop[j + kPre] = a_read(j + kPre);
+      if (j + kPre >= NA) cop[j + kPre - NA] = c_read(j + kPre - NA);
+      if (j == kPre) ld_read(0);
+      if (j == NA / 2 + kPre) ld_read(1);
+      const int mt = j / (2 * NKK), kk = (j / 2) % NKK;
+      if (j & 1) dpv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[j], vf[kk], dpv[mt], 0, 0, 0);
+      else s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[j], kf[kk], s[mt], 0, 0, 0);
+      // half 0 is complete after MFMA NA/2 - 1: its 16 values are processed
+      // beside the MFMAs of half 1, EA per MFMA
+      if (j >= NA / 2) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const float4 lv = *reinterpret_cast<const float4*>(lsep + 32 * mt + 8 * g4 + 4 * hh);
-          const float4 dv = *reinterpret_cast<const float4*>(dp + 32 * mt + 8 * g4 + 4 * hh);
-          const float la[4] = {lv.x, lv.y, lv.z, lv.w};
-          const float da[4] = {dv.x, dv.y, dv.z, dv.w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int r = 4 * g4 + u;
-            float sv = s[mt][r];
-            if constexpr (decltype(masked)::value) {
-              const int qrow = q0 + 32 * mt + 8 * g4 + 4 * hh + u;
-              if (!(key_ok && qrow < c && visible(key - qrow, delta))) sv = -INFINITY;
-            }
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c2, -la[u]));
-            s[mt][r] = p;
-            dpv[mt][r] = p * (dpv[mt][r] - da[u]);
-          }
-        }
-      bf16x8 pa[4], dsa[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pa[kk][j] = (__bf16)s[kk >> 1][8 * (kk & 1) + j];
-          dsa[kk][j] = (__bf16)dpv[kk >> 1][8 * (kk & 1) + j];
-        }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          acc_dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], T::tr(os, 16 * kk, 32 * dt, lane), acc_dv[dt], 0, 0, 0);
-          acc_dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsa[kk], T::tr(qs, 16 * kk, 32 * dt, lane), acc_dk[dt], 0, 0, 0);
-        }
+        for (int e = 0; e < EA; ++e) softmax_elem(0, (j - NA / 2) * EA + e);
+      }
+      __builtin_amdgcn_sched_barrier(0);         // keep each slot's reads kPre MFMAs ahead
     }
-    if (it + 1 < n_iter) store_ld(it + 1);
-    dma_wait();
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      if (j + kPre < NC) cop[j + kPre] = c_read(j + kPre);
+      const int kk = j / (2 * NDT), dt = (j / 2) % NDT;
+      if (j & 1) acc_dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsa[kk], cop[j], acc_dk[dt], 0, 0, 0);
+      else acc_dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], cop[j], acc_dv[dt], 0, 0, 0);
+      // the first NC/2 MFMAs use half 0 only: half 1's softmax runs beside them
+      if (j < NC / 2) {
+#pragma unroll
+        for (int e = 0; e < EC; ++e) softmax_elem(1, j * EC + e);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto step = [&](int it, auto masked) {
+    if (it + NS - 1 < n_iter) issue(it + NS - 1);        // into the stage read in iteration it - 1
+    if constexpr (decltype(masked)::value) {
+      // keys [kw0, kw0+32) against queries [q0, q0+64): skip when none is visible
+      const int q0 = (qt0 + it / group) * kTile;
+      if ((kw0 < c) && visible(kw0 - (q0 + kTile - 1), delta)) compute(it, masked);
+    } else {
+      compute(it, masked);
+    }
+    if (it + 1 < n_iter) wait_tile(it + 1, min(it + NS - 1, n_iter - 1));
     __syncthreads();
   };
 
-  if (n_iter > 0) {
-    issue(0);
-    store_ld(0);
-    dma_wait();
-  }
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (i < n_iter) issue(i);
+  if (n_iter > 0) wait_tile(0, min(NS - 2, n_iter - 1));
   __syncthreads();
   // Query tiles run in order (heads of the group innermost); tile qt needs no
   // per-element mask when every pair of this workgroup is visible and in
@@ -331,7 +340,7 @@ void dkdv_kernel(BwdArgs a) {
 template <int D, int HPW>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(RA_DQ_WAVES, RA_DQ_WAVES)))
 void dq_kernel(BwdArgs a) {
-  using T = STile<D>;
+  using T = tile::STile<D>;
   constexpr int WPH = 4 / HPW;
   constexpr int ROWS = 32 * WPH;
   constexpr int NKK = D / 16;

@@ -37,6 +37,7 @@
 #include <type_traits>
 
 #include "ra_internal.h"
+#include "ra_tile.h"
 
 #ifndef RA_FWD_WAVES
 #define RA_FWD_WAVES 2   // waves per SIMD the forward kernel is built for
@@ -59,46 +60,20 @@ __device__ inline int xcd_remap(int L, int T) {
   return (L % 8) * (T / 8) + (L / 8);
 }
 
-__device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Raw buffer resource over [p, p + nbytes): loads beyond nbytes return 0 (and
-// LDS-DMA loads beyond it write 0), so rows past the end of a block read as
-// zeros without branches.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int nbytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, nbytes, 0x00020000);
-}
-__device__ inline uint4 bload16(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-// 16-byte LDS-DMA load: lane L's 16 bytes from r + voff land at lds + 16 L.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
-}
+using tile::as_bf16x8;
+using tile::bload16;
 
 // Lazy rescaling threshold (log2 units): the running reference max only moves
 // when a row's max grows by more than this, so P = 2^(s - m_ref) <= 2^8.
 constexpr float kRescaleThreshold = 8.0f;
 
-// K and V tiles of 64 keys live in LDS unpadded (rows of 2*D bytes) with the
-// 16-byte chunks of each row XOR-swizzled, filled by LDS-DMA buffer loads
-// (each lane's 16 bytes land at base + 16 * lane, so the swizzle is applied
-// by choosing which global chunk each lane fetches):
-//   K: LDS chunk C of row R holds global chunk C ^ (R % 8)  -> the score MFMA's
-//      A reads (rows 0..7 of a lane group, same chunk) hit distinct banks;
-//   V: LDS chunk C of row R holds global chunk C ^ 2 (R % 4) -> the transposing
-//      reads below (4 rows x 32 bytes per 16-lane group) hit distinct banks.
+// K and V tiles of 64 keys are staged by LDS-DMA into the swizzled row-major
+// layout of ra_tile.h: K is read by rows (A operand of the score MFMA), V by
+// transposing reads (A operand of O^T += V^T P^T).
 template <int D>
 struct FwdTile {
-  static constexpr int ROWB = 2 * D;                 // bytes per row
-  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  static constexpr int TILE = kBN * ROWB;            // bytes per tile
-  static constexpr int DMA_PER_WAVE = kBN * CPR / 64 / 4;   // DMA instructions per wave per tile
+  using S = tile::STile<D>;
+  static constexpr int TILE = S::BYTES;              // bytes per 64-row tile
   static constexpr int BYTES = 4 * TILE;             // K[2], V[2]
 };
 
@@ -151,9 +126,9 @@ void fwd_bf16_kernel(FwdArgs a) {
                      ((int64_t)(b * a.hkv + kvh) * c) * D;
   const __bf16* vp = reinterpret_cast<const __bf16*>(a.v) + host * a.kv_host_stride +
                      ((int64_t)(b * a.hkv + kvh) * c) * D;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qp, blk_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp, blk_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vp, blk_bytes);
+  const __amdgpu_buffer_rsrc_t rq = tile::rsrc(qp, blk_bytes);
+  const __amdgpu_buffer_rsrc_t rk = tile::rsrc(kp, blk_bytes);
+  const __amdgpu_buffer_rsrc_t rv = tile::rsrc(vp, blk_bytes);
   float* mp = a.m + host * a.ml_host_stride + (int64_t)(b * a.hq + head) * c;
   float* lp = a.l + host * a.ml_host_stride + (int64_t)(b * a.hq + head) * c;
   float* op = a.o + host * a.q_host_stride + ((int64_t)(b * a.hq + head) * c) * D;
@@ -186,53 +161,20 @@ void fwd_bf16_kernel(FwdArgs a) {
   }
   float m_true = m_ref;
 
-  // ---- LDS-DMA tile loads ----
-  // DMA instruction i of this wave fills LDS bytes [(wave*DPW + i) * 1024, +1024)
-  // of the tile: lane L writes LDS row R = idx / CPR, chunk C = idx % CPR with
-  // idx = (wave*DPW + i) * 64 + L, fetching global chunk C ^ swizzle(R).
-  // Row R = (wave*DPW + i) * RPI + lane / CPR (RPI = 64 / CPR rows per
-  // instruction, a multiple of 4), so R % 4 depends on the lane only and R % 8
-  // on the lane and the parity of wave*DPW + i.
-  constexpr int RPI = 64 / T::CPR;
-  const int lrow = lane / T::CPR, lch = lane % T::CPR;
-  const int lane_off = lrow * T::ROWB;
-  int kx[2];
-#pragma unroll
-  for (int p = 0; p < 2; ++p) kx[p] = (lch ^ ((RPI * p + lrow) & 7)) * 16;
-  const int vx = (lch ^ (2 * (lrow & 3))) * 16;
-  auto dma_k = [&](int t, int buf) {
-    unsigned char* base = smem + buf * T::TILE;
-#pragma unroll
-    for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
-      const int ins = wave * T::DMA_PER_WAVE + i;
-      dma16(rk, base + ins * 1024, t * T::TILE + ins * RPI * T::ROWB + lane_off + kx[ins & 1]);
-    }
-  };
-  auto dma_v = [&](int t, int buf) {
-    unsigned char* base = smem + (2 + buf) * T::TILE;
-#pragma unroll
-    for (int i = 0; i < T::DMA_PER_WAVE; ++i) {
-      const int ins = wave * T::DMA_PER_WAVE + i;
-      dma16(rv, base + ins * 1024, t * T::TILE + ins * RPI * T::ROWB + lane_off + vx);
-    }
-  };
-  auto dma_wait = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
-
-  // ---- per-lane LDS read offsets ----
-  // scores: A operand row R = 32mt + l32, global chunk 2kk + hh, swizzle R % 8 = l32 % 8
-  const int ksw = l32 & 7;
-  // P V: transposing read r of K-step kk, d tile dt.  In each 16-lane group
-  // (G = lane / 16, j = lane % 16) lane j addresses row 16kk + 8r + 4h + j/4
-  // (h = G / 2) at columns 32dt + 16(G % 2) + 4(j % 4) .. +3; lane i of the
-  // group then receives column 32dt + 16(G % 2) + i of those four rows.
-  const int G = lane >> 4, jj = lane & 15;
-  const int va = jj & 3, vk = jj >> 2, vh = G >> 1, vdh = G & 1;
-  int v_off[NDT];
+  // ---- LDS-DMA tile loads and per-lane LDS read offsets ----
+  using S = typename T::S;
+  auto dma_k = [&](int t, int buf) { S::dma(rk, smem + buf * T::TILE, t * kBN, wave, lane); };
+  auto dma_v = [&](int t, int buf) { S::dma(rv, smem + (2 + buf) * T::TILE, t * kBN, wave, lane); };
+  // scores: A operand row R = 32mt + l32 (swizzle depends on R % 16 only),
+  // global chunk 2kk + hh
+  const int ksw = tile::swz<D>(l32);
+  // P V: transposing reads over rows 16kk.. of the V tile; the swizzle depends
+  // on the row mod 16, so the offsets for kk = 0 serve every kk
+  int v_lo[NDT], v_hi[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
-    const int row = 4 * vh + vk;                       // + 16kk + 8r (immediates)
-    const int chunk = 4 * dt + 2 * vdh + (va >> 1);
-    v_off[dt] = row * T::ROWB + ((chunk ^ (2 * vk)) * 16) + 8 * (va & 1);
+    v_lo[dt] = S::tr_off(0, 32 * dt, lane);
+    v_hi[dt] = S::tr_off(8, 32 * dt, lane);
   }
 
   auto scores = [&](int buf, f32x16 (&s)[2]) {
@@ -246,7 +188,7 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         const int R = 32 * mt + l32;
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + R * T::ROWB + (((2 * kk + hh) ^ ksw) * 16));
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + R * S::ROWB + (((2 * kk + hh) ^ ksw) * 16));
         s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[mt], 0, 0, 0);
       }
   };
@@ -256,13 +198,8 @@ void fwd_bf16_kernel(FwdArgs a) {
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vs + v_off[dt] + (16 * kk) * T::ROWB));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(vs + v_off[dt] + (16 * kk + 8) * T::ROWB));
-        typedef short i16x8 __attribute__((ext_vector_type(8)));
-        const i16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pb[kk], acc_o[dt], 0, 0, 0);
+        const bf16x8 va = S::tr_at(vs + (16 * kk) * S::ROWB, v_lo[dt], v_hi[dt]);
+        acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kk], acc_o[dt], 0, 0, 0);
       }
   };
   // masked row max of a score tile (base-2 units, combined over the two lane halves)
@@ -320,7 +257,7 @@ void fwd_bf16_kernel(FwdArgs a) {
   // t+1 into the other K/V buffers (last read in iteration t-1) overlaps it.
   dma_k(0, 0);
   dma_v(0, 0);
-  dma_wait();
+  tile::dma_wait();
   __syncthreads();
   auto step = [&](int t, auto masked) {
     if (t + 1 < ntiles) {
@@ -341,7 +278,7 @@ void fwd_bf16_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    dma_wait();
+    tile::dma_wait();
     __syncthreads();
   };
   for (int t = 0; t < n_unmasked; ++t) step(t, std::false_type{});

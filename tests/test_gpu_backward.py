@@ -71,19 +71,21 @@ def _gather(t, rows, heads=None):
 
 
 SMALL = [
-    # (hq, hkv, layout, mask, N, c)
-    (2, 2, C, 0, 3, 200),
-    (2, 2, C, 1, 4, 130),
-    (4, 2, S, 1, 3, 96),
-    (4, 1, C, 1, 2, 257),
-    (2, 2, S, 1, 4, 64),
+    # (hq, hkv, d, layout, mask, N, c)
+    (2, 2, 128, C, 0, 3, 200),
+    (2, 2, 128, C, 1, 4, 130),
+    (4, 2, 128, S, 1, 3, 96),
+    (4, 1, 128, C, 1, 2, 257),
+    (2, 2, 128, S, 1, 4, 64),
+    (2, 2, 64, C, 0, 2, 300),
+    (4, 2, 64, S, 1, 3, 129),
 ]
 
 
-@pytest.mark.parametrize("hq,hkv,layout,mask,N,c", SMALL)
-def test_ring_bwd_small_all_rows(torch, hq, hkv, layout, mask, N, c):
+@pytest.mark.parametrize("hq,hkv,d,layout,mask,N,c", SMALL)
+def test_ring_bwd_small_all_rows(torch, hq, hkv, d, layout, mask, N, c):
     import long_context_transformers_amd as ra
-    w = rs.Workload("bwd_small", 95, 1, hq, hkv, 128, N, c, rs.DT_BF16, mask, layout, 0, N)
+    w = rs.Workload("bwd_small", 95, 1, hq, hkv, d, N, c, rs.DT_BF16, mask, layout, 0, N)
     inp = rs.make_inputs(w, with_do=True)
     q, k, v, do = (H.dev_tensor(x, w.dtype) for x in (inp.q_dev, inp.k_dev, inp.v_dev, inp.do_dev))
     O, lse = _fwd(torch, w, q, k, v)
@@ -98,7 +100,7 @@ def test_ring_bwd_small_all_rows(torch, hq, hkv, layout, mask, N, c):
     assert stats["compute_steps"] == N and stats["transfers"] == N - 1
     rows = np.arange(c)
     dQr, dKr, dVr = _oracle_grads(w, inp, rows, rows, range(hkv))
-    tag = f"{hq}/{hkv} layout={layout} mask={mask} N={N} c={c}"
+    tag = f"{hq}/{hkv} d={d} layout={layout} mask={mask} N={N} c={c}"
     _compare(f"ring_bwd dQ {tag}", _gather(dQ, rows), dQr)
     _compare(f"ring_bwd dK {tag}", _gather(dK, rows), dKr)
     _compare(f"ring_bwd dV {tag}", _gather(dV, rows), dVr)
