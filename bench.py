@@ -251,9 +251,8 @@ def elementwise_bw(torch, ra, reps=10):
 
 def reference_gemm(torch, n=8192, reps=20):
     """This GPU's bf16 GEMM rate (torch.matmul, n^3, N(0,1) operands): a
-    measured ceiling for dense bf16 contractions on random data, beside the
-    published peak (matrix-core throughput on this part drops with random
-    operand data, so the published peak is not reachable by real inputs)."""
+    measured practical ceiling for dense bf16 contractions on random data,
+    reported beside the published peak."""
     g = torch.Generator(device="cuda")
     g.manual_seed(1234)
     a = torch.randn((n, n), device="cuda", dtype=torch.bfloat16, generator=g)

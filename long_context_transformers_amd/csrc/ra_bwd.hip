@@ -41,7 +41,7 @@
 #define RA_DKDV_STAGES 4   // LDS stages of the dK/dV kernel's query-tile pipeline (3 or 4)
 #endif
 #ifndef RA_DKDV_PREFETCH
-#define RA_DKDV_PREFETCH 3   // MFMAs by which the dK/dV kernel's LDS operand reads run ahead
+#define RA_DKDV_PREFETCH 2   // slots (4 MFMAs each) by which the dK/dV kernel's LDS operand reads run ahead
 #endif
 
 namespace ra {
@@ -72,10 +72,10 @@ __device__ inline int xcd_remap_b(int L, int T) {
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void dkdv_kernel(BwdArgs a) {
-  using T = tile::STile<D>;
-  constexpr int NKK = D / 16;
-  constexpr int NDT = D / 32;
-  constexpr int BK = 128;                                  // keys per workgroup
+  using T = tile::STile<D, tile::kSwz16>;
+  constexpr int NKK = D / 32;                              // 32-deep d steps of S, dP
+  constexpr int NT = D / 16;                               // 16-wide d tiles of dK, dV
+  constexpr int BK = 128;                                  // keys per workgroup (4 waves x 32)
   constexpr int BUF = 2 * T::BYTES + 2 * kTile * 4;        // Q, dO, lse, D of one query tile
   constexpr int NS = RA_DKDV_STAGES;                       // LDS stages (tiles in flight + 1)
   constexpr int NV = 2 * T::DPW + 1;                       // DMA instructions per wave per tile
@@ -96,32 +96,38 @@ void dkdv_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int k0 = kt * BK;
-  const int kw0 = k0 + 32 * wave;                          // this wave's first key
-  const int key = kw0 + l32;                               // this lane's key
-  const bool key_ok = key < c;
+  const int kw0 = k0 + 32 * wave;                          // this wave's keys: sub-tiles of 16
   const int blk_bytes = c * D * 2;
 
   const int64_t kvoff = host * a.kv_host_stride + ((int64_t)(b * a.hkv + kvh) * c) * D;
   const __amdgpu_buffer_rsrc_t rk = rsrc(reinterpret_cast<const __bf16*>(a.k) + kvoff, blk_bytes);
   const __amdgpu_buffer_rsrc_t rv = rsrc(reinterpret_cast<const __bf16*>(a.v) + kvoff, blk_bytes);
 
-  // K^T and V^T fragments (B operands): lane = key, items = d 16kk + 8hh + j
-  bf16x8 kf[NKK], vf[NKK];
+  // K^T and V^T fragments (B operands of S and dP): sub-tile ks, d step kk,
+  // lane (g, i) holds d 32kk + 8g .. +7 of key kw0 + 16ks + i.
+  bf16x8 kf[2][NKK], vf[2][NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    kf[kk] = as_bf16x8(bload16(rk, (key * D + 16 * kk + 8 * hh) * 2));
-    vf[kk] = as_bf16x8(bload16(rv, (key * D + 16 * kk + 8 * hh) * 2));
-  }
-  f32x16 acc_dk[NDT], acc_dv[NDT];
+  for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      acc_dk[dt][r] = 0.f;
-      acc_dv[dt][r] = 0.f;
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int kr = kw0 + 16 * ks + l16;
+      kf[ks][kk] = as_bf16x8(bload16(rk, (kr * D + 32 * kk + 8 * g) * 2));
+      vf[ks][kk] = as_bf16x8(bload16(rv, (kr * D + 32 * kk + 8 * g) * 2));
     }
+  // dK, dV accumulators: sub-tile ks, d tile nt; value r of lane (g, i) is
+  // key kw0 + 16ks + 4g + r, d column 16nt + i.
+  f32x4 acc_dk[2][NT], acc_dv[2][NT];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        acc_dk[ks][nt][r] = 0.f;
+        acc_dv[ks][nt][r] = 0.f;
+      }
 
   // queries that can see a key of this workgroup: q >= k0 - delta
   const int q_start = max(0, k0 - delta);
@@ -156,30 +162,29 @@ void dkdv_kernel(BwdArgs a) {
     else tile::vm_wait<0>();
   };
 
-  // Loop-invariant LDS offsets.  Row reads: row R = 32mt + l32 (the swizzle
-  // depends on R mod 16 only), global chunk 2kk + hh.  Transposing reads: the
-  // two halves of the operand for d tile dt at rows 16kk.. .
+  // Loop-invariant LDS offsets.  Row reads: row 16mt + i of a tile (the
+  // swizzle depends on the row mod 16 only), global chunk 4kk + g.
+  // Transposing reads: d tile nt at tile rows 0.. (see STile::tr16_off).
   int roff[NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) roff[kk] = l32 * T::ROWB + (((2 * kk + hh) ^ tile::swz<D>(l32)) * 16);
-  int tlo[NDT], thi[NDT];
+  for (int kk = 0; kk < NKK; ++kk) roff[kk] = l16 * T::ROWB + (((4 * kk + g) ^ tile::swz<D, tile::kSwz16>(l16)) * 16);
+  int toff[NT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    tlo[dt] = T::tr_off(0, 32 * dt, lane);
-    thi[dt] = T::tr_off(8, 32 * dt, lane);
-  }
-  auto rowa = [&](const unsigned char* t, int mt, int kk) {
-    return *reinterpret_cast<const bf16x8*>(t + 32 * mt * T::ROWB + roff[kk]);
-  };
+  for (int nt = 0; nt < NT; ++nt) toff[nt] = T::tr16_off(16 * nt, lane);
 
   const float c2 = a.scale_log2;
-  // One query tile against this wave's 32 keys.  Phases, in issue order:
-  //  A  S = Q K^T and dP = dO V^T, query half mt = 0 then mt = 1 (S and dP
-  //     chains alternate, so consecutive MFMAs are independent);
-  //  B  P = 2^(S c2 - lse2), dS = P (dP - D) for half 0 while the MFMAs of
-  //     half 1 run, then for half 1 while the first dV/dK MFMAs run;
-  //  C  dV += P^T dO, dK += dS^T Q (transposing reads of the same tiles).
-  // LDS reads are kept two to three MFMAs ahead of their use.
+  // One query tile (64 rows = 4 MFMA row tiles mt) against this wave's 32
+  // keys, with v_mfma_f32_16x16x32_bf16.  Phases, in issue order:
+  //  A  S = Q K^T and dP = dO V^T: slot u = (mt, kk) reads one Q row operand
+  //     and one dO row operand and feeds four MFMAs (both key sub-tiles);
+  //  B  P = 2^(S c2 - lse2), dS = P (dP - D): the 16 values of query rows
+  //     0..31 (half 0) run beside the MFMAs of rows 32..63, those of half 1
+  //     beside the first dV/dK MFMAs (which use half 0 only);
+  //  C  dV += P^T dO, dK += dS^T Q over query steps kq (32 rows = half kq):
+  //     slot v = (kq, nt) reads the transposed dO and Q operands and feeds
+  //     four MFMAs.  P^T's item j of lane (g, i) is query 32kq + 16(j/4) +
+  //     4g + j%4, the order in which the transposing reads deliver dO and Q.
+  // Operand reads run kPre slots ahead, pinned by sched_barrier.
   auto compute = [&](int it, auto masked) {
     const int q0 = (qt0 + it / group) * kTile;
     const unsigned char* base = smem + (it % NS) * BUF;
@@ -187,89 +192,86 @@ void dkdv_kernel(BwdArgs a) {
     const unsigned char* os = base + T::BYTES;
     const float* lsep = reinterpret_cast<const float*>(base + 2 * T::BYTES);
     const float* dp = lsep + kTile;
-    f32x16 s[2], dpv[2];
+    f32x4 s[4][2], dpv[4][2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[mt][r] = 0.f;
-        dpv[mt][r] = 0.f;
-      }
-    // A: MFMA j of 4 NKK: half mt = j / (2 NKK), d step kk = (j / 2) % NKK,
-    // S (j even) or dP (j odd); operands read kPre MFMAs ahead.
-    constexpr int NA = 4 * NKK, kPre = RA_DKDV_PREFETCH;
-    auto a_read = [&](int j) {
-      return rowa((j & 1) ? os : qs, j / (2 * NKK), (j / 2) % NKK);
-    };
-    // C: MFMA j of 8 NDT: kk = j / (2 NDT), dt = (j / 2) % NDT, dV (j even)
-    // or dK (j odd); transposing operand reads kPre MFMAs ahead.
-    constexpr int NC = 8 * NDT;
-    auto c_read = [&](int j) {
-      const int kk = j / (2 * NDT), dt = (j / 2) % NDT;
-      return T::tr_at(((j & 1) ? qs : os) + 16 * kk * T::ROWB, tlo[dt], thi[dt]);
-    };
-    // B, one element at a time: value r of half mt belongs to query
-    // 32mt + 8(r/4) + 4hh + r%4 and lands in item r%8 of pa/dsa[2mt + r/8].
-    float la[2][16], da[2][16];
-    auto ld_read = [&](int mt) {
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        // one typed vector load each (keeps the load's alias information, see ra_tile.h)
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(lsep + 32 * mt + 8 * g4 + 4 * hh);
-        const f32x4 dv = *reinterpret_cast<const f32x4*>(dp + 32 * mt + 8 * g4 + 4 * hh);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          la[mt][4 * g4 + u] = lv[u] * kBwdLog2e;   // lse in base 2
-          da[mt][4 * g4 + u] = dv[u];
+        for (int r = 0; r < 4; ++r) {
+          s[mt][ks][r] = 0.f;
+          dpv[mt][ks][r] = 0.f;
         }
-      }
+    constexpr int NU = 4 * NKK, NC = 2 * NT, kPre = RA_DKDV_PREFETCH;
+    bf16x8 qa[NU], oa[NU], ob[NC], qb[NC];
+    auto a_read = [&](int u) {
+      const int mt = u / NKK, kk = u % NKK;
+      qa[u] = *reinterpret_cast<const bf16x8*>(qs + 16 * mt * T::ROWB + roff[kk]);
+      oa[u] = *reinterpret_cast<const bf16x8*>(os + 16 * mt * T::ROWB + roff[kk]);
     };
-    bf16x8 pa[4], dsa[4];
-    // (every row of an unmasked tile sees a key, so its lse is finite; in a
-    // masked tile, invisible pairs, which include every pair of a row that
-    // sees no key at all, get P = 0 by selection)
-    auto softmax_elem = [&](int mt, int r) {
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][r], c2, -la[mt][r]));
+    auto c_read = [&](int v) {
+      const int kq = v / NT, nt = v % NT;
+      ob[v] = T::tr_at(os + 32 * kq * T::ROWB, toff[nt], toff[nt] + 16 * T::ROWB);
+      qb[v] = T::tr_at(qs + 32 * kq * T::ROWB, toff[nt], toff[nt] + 16 * T::ROWB);
+    };
+    // lse (base 2) and D of query rows 16mt + 4g + 0..3, one typed vector load
+    // each (keeps the load's alias information, see ra_tile.h)
+    f32x4 la[4], da[4];
+    auto ld_read = [&](int mt) {
+      la[mt] = *reinterpret_cast<const f32x4*>(lsep + 16 * mt + 4 * g) * kBwdLog2e;
+      da[mt] = *reinterpret_cast<const f32x4*>(dp + 16 * mt + 4 * g);
+    };
+    // value e of half hf: sub-tile ks = e / 8, row tile mt = 2hf + (e / 4) % 2,
+    // r = e % 4; it lands in item 4 ((e / 4) % 2) + r of pa/dsa[ks][hf].
+    // (Every row of an unmasked tile sees a key, so its lse is finite; in a
+    // masked tile invisible pairs, including all pairs of a row that sees no
+    // key at all, get P = 0 by selection.)
+    bf16x8 pa[2][2], dsa[2][2];
+    auto softmax_elem = [&](int hf, int e) {
+      const int ks = e >> 3, mh = (e >> 2) & 1, r = e & 3, mt = 2 * hf + mh;
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][ks][r], c2, -la[mt][r]));
       if constexpr (decltype(masked)::value) {
-        const int qrow = q0 + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (!(key_ok && qrow < c && visible(key - qrow, delta))) p = 0.f;
+        const int key = kw0 + 16 * ks + l16;
+        const int qrow = q0 + 16 * mt + 4 * g + r;
+        const bool vis = (key < c) & (qrow < c) & visible(key - qrow, delta);
+        p = vis ? p : 0.f;
       }
-      pa[2 * mt + (r >> 3)][r & 7] = (__bf16)p;
-      dsa[2 * mt + (r >> 3)][r & 7] = (__bf16)(p * (dpv[mt][r] - da[mt][r]));
+      pa[ks][hf][4 * mh + r] = (__bf16)p;
+      dsa[ks][hf][4 * mh + r] = (__bf16)(p * (dpv[mt][ks][r] - da[mt][r]));
     };
+    constexpr int EA = 16 / (NU / 2), EC = 16 / (NC / 2);   // softmax values per slot
+    static_assert(EA * (NU / 2) == 16 && EC * (NC / 2) == 16, "slots must divide a half's 16 values");
 
-    constexpr int EA = 16 / (NA / 2), EC = 16 / (NC / 2);   // softmax values per MFMA slot
-    static_assert(EA * (NA / 2) == 16 && EC * (NC / 2) == 16, "slots must divide a half's 16 values");
-    bf16x8 aop[NA], cop[NC];
 #pragma unroll
-    for (int j = 0; j < kPre; ++j) aop[j] = a_read(j);
+    for (int u = 0; u < kPre; ++u) a_read(u);
 #pragma unroll
-    for (int j = 0; j < NA; ++j) {
-      if (j + kPre < NA) aop[j + kPre] = a_read(j + kPre);
-      if (j + kPre >= NA) cop[j + kPre - NA] = c_read(j + kPre - NA);
-      if (j == kPre) ld_read(0);
-      if (j == NA / 2 + kPre) ld_read(1);
-      const int mt = j / (2 * NKK), kk = (j / 2) % NKK;
-      if (j & 1) dpv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[j], vf[kk], dpv[mt], 0, 0, 0);
-      else s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[j], kf[kk], s[mt], 0, 0, 0);
-      // half 0 is complete after MFMA NA/2 - 1: its 16 values are processed
-      // beside the MFMAs of half 1, EA per MFMA
-      if (j >= NA / 2) {
+    for (int u = 0; u < NU; ++u) {
+      if (u + kPre < NU) a_read(u + kPre);
+      else c_read(u + kPre - NU);
+      if (u == 0) { ld_read(0); ld_read(1); }
+      if (u == NU / 2) { ld_read(2); ld_read(3); }
+      const int mt = u / NKK, kk = u % NKK;
+      s[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[u], kf[0][kk], s[mt][0], 0, 0, 0);
+      s[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[u], kf[1][kk], s[mt][1], 0, 0, 0);
+      dpv[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa[u], vf[0][kk], dpv[mt][0], 0, 0, 0);
+      dpv[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa[u], vf[1][kk], dpv[mt][1], 0, 0, 0);
+      if (u >= NU / 2) {                         // half 0 (row tiles 0, 1) is complete
 #pragma unroll
-        for (int e = 0; e < EA; ++e) softmax_elem(0, (j - NA / 2) * EA + e);
+        for (int e = 0; e < EA; ++e) softmax_elem(0, (u - NU / 2) * EA + e);
       }
-      __builtin_amdgcn_sched_barrier(0);         // keep each slot's reads kPre MFMAs ahead
+      __builtin_amdgcn_sched_barrier(0);         // keep each slot's reads kPre slots ahead
     }
 #pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      if (j + kPre < NC) cop[j + kPre] = c_read(j + kPre);
-      const int kk = j / (2 * NDT), dt = (j / 2) % NDT;
-      if (j & 1) acc_dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsa[kk], cop[j], acc_dk[dt], 0, 0, 0);
-      else acc_dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kk], cop[j], acc_dv[dt], 0, 0, 0);
-      // the first NC/2 MFMAs use half 0 only: half 1's softmax runs beside them
-      if (j < NC / 2) {
+    for (int v = 0; v < NC; ++v) {
+      if (v + kPre < NC) c_read(v + kPre);
+      const int kq = v / NT, nt = v % NT;
+      acc_dv[0][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[0][kq], ob[v], acc_dv[0][nt], 0, 0, 0);
+      acc_dv[1][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[1][kq], ob[v], acc_dv[1][nt], 0, 0, 0);
+      acc_dk[0][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsa[0][kq], qb[v], acc_dk[0][nt], 0, 0, 0);
+      acc_dk[1][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsa[1][kq], qb[v], acc_dk[1][nt], 0, 0, 0);
+      if (v < NC / 2) {                          // slots of kq = 0: half 1's softmax beside them
 #pragma unroll
-        for (int e = 0; e < EC; ++e) softmax_elem(1, j * EC + e);
+        for (int e = 0; e < EC; ++e) softmax_elem(1, v * EC + e);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -308,30 +310,57 @@ void dkdv_kernel(BwdArgs a) {
   for (int it = it_a; it < it_b; ++it) step(it, std::false_type{});
   for (int it = it_b; it < n_iter; ++it) step(it, std::true_type{});
 
-  // epilogue: out = in + contribution (scale on dK); lane = d column, value r = key
-  const int out_host = (host + a.dkv_out_host_shift) % a.n_hosts;
-  const int64_t ooff = out_host * a.dkv_out_host_stride + ((int64_t)(b * a.hkv + kvh) * c) * D;
-  const int64_t ioff = host * a.dkv_in_host_stride + ((int64_t)(b * a.hkv + kvh) * c) * D;
-  float* dko = a.dk_out + ooff;
-  float* dvo = a.dv_out + ooff;
-  const float* dki = a.dk_in ? a.dk_in + ioff : nullptr;
-  const float* dvi = a.dv_in ? a.dv_in + ioff : nullptr;
+  // epilogue: out = in + contribution (scale on dK).  The accumulators are
+  // staged through the (idle) LDS stages as row-major fp32 [BK keys][D] for
+  // dK then dV, so the read of the partial sum and the store run as
+  // contiguous 16-byte accesses.  No LDS-DMA is in flight here: the last
+  // iteration waited for every issued tile.
+  static_assert(2 * BK * D * 4 <= NS * BUF, "epilogue staging must fit in the LDS stages");
+  float* st = reinterpret_cast<float*>(smem);
   const float scale = a.scale;
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
+  for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kr = kw0 + (r >> 2) * 8 + 4 * hh + (r & 3);
-      if (kr < c) {
-        const int64_t o = (int64_t)kr * D + 32 * dt + l32;
-        float vk = scale * acc_dk[dt][r];
-        float vv = acc_dv[dt][r];
-        if (dki) vk += dki[o];
-        if (dvi) vv += dvi[o];
-        dko[o] = vk;
-        dvo[o] = vv;
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kr = 32 * wave + 16 * ks + 4 * g + r;      // key row within the workgroup
+        st[kr * D + 16 * nt + l16] = scale * acc_dk[ks][nt][r];
+        st[BK * D + kr * D + 16 * nt + l16] = acc_dv[ks][nt][r];
+      }
+  __syncthreads();
+  const int out_host = (host + a.dkv_out_host_shift) % a.n_hosts;
+  const int64_t ooff = out_host * a.dkv_out_host_stride + ((int64_t)(b * a.hkv + kvh) * c + k0) * D;
+  const int64_t ioff = host * a.dkv_in_host_stride + ((int64_t)(b * a.hkv + kvh) * c + k0) * D;
+  const int valid = min(BK, c - k0) * D;                     // floats of this workgroup's keys
+  constexpr int V4 = BK * D / 4 / kBwdThreads;              // float4 per thread per matrix
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    float* out = (m == 0 ? a.dk_out : a.dv_out) + ooff;
+    const float* in = (m == 0 ? a.dk_in : a.dv_in);
+    float4 v[V4];
+#pragma unroll
+    for (int j = 0; j < V4; ++j) {
+      const int e = 4 * (j * kBwdThreads + tid);
+      v[j] = *reinterpret_cast<const float4*>(st + m * BK * D + e);
+    }
+    if (in) {
+      in += ioff;
+#pragma unroll
+      for (int j = 0; j < V4; ++j) {
+        const int e = 4 * (j * kBwdThreads + tid);
+        if (e < valid) {
+          const float4 o = *reinterpret_cast<const float4*>(in + e);
+          v[j].x += o.x; v[j].y += o.y; v[j].z += o.z; v[j].w += o.w;
+        }
       }
     }
+#pragma unroll
+    for (int j = 0; j < V4; ++j) {
+      const int e = 4 * (j * kBwdThreads + tid);
+      if (e < valid) *reinterpret_cast<float4*>(out + e) = v[j];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -340,11 +369,11 @@ void dkdv_kernel(BwdArgs a) {
 template <int D, int HPW>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(RA_DQ_WAVES, RA_DQ_WAVES)))
 void dq_kernel(BwdArgs a) {
-  using T = tile::STile<D>;
+  using T = tile::STile<D, tile::kSwz16>;
   constexpr int WPH = 4 / HPW;
   constexpr int ROWS = 32 * WPH;
-  constexpr int NKK = D / 16;
-  constexpr int NDT = D / 32;
+  constexpr int NKK = D / 32;                              // 32-deep d steps of S^T, dP^T
+  constexpr int NT = D / 16;                               // 16-row d tiles of dQ^T
   constexpr int BUF = 2 * T::BYTES;                        // K, V
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * BUF];
 
@@ -362,13 +391,11 @@ void dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int head = hg * HPW + wave / WPH;
   const int kvh = head / (a.hq / a.hkv);
   const int q0 = rt * ROWS;
-  const int qw0 = q0 + (wave % WPH) * 32;
-  const int qr = qw0 + l32;
-  const bool row_ok = qr < c;
+  const int qw0 = q0 + (wave % WPH) * 32;                  // this wave's rows: sub-tiles of 16
   const int row_last = min(q0 + ROWS, c) - 1;
   const int kend = min(c, row_last + delta + 1);
   const int ntiles = kend > 0 ? (kend + kTile - 1) / kTile : 0;
@@ -386,25 +413,57 @@ void dq_kernel(BwdArgs a) {
   const int64_t so = host * a.ml_host_stride + (int64_t)(b * a.hq + head) * c;
   float* dqp = a.dq + qoff;
 
-  bf16x8 qf[NKK], of[NKK];
+  // Q^T and dO^T fragments (B operands of S^T and dP^T): sub-tile qs, d step
+  // kk, lane (g, i) holds d 32kk + 8g .. +7 of row qw0 + 16qs + i; that row's
+  // lse (base 2; +inf for a row without keys, so P = 0) and D.
+  bf16x8 qf[2][NKK], of[2][NKK];
+  float lse2[2], Dq[2];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    qf[kk] = as_bf16x8(bload16(rq, (qr * D + 16 * kk + 8 * hh) * 2));
-    of[kk] = as_bf16x8(bload16(ro, (qr * D + 16 * kk + 8 * hh) * 2));
+  for (int qs = 0; qs < 2; ++qs) {
+    const int qr = qw0 + 16 * qs + l16;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      qf[qs][kk] = as_bf16x8(bload16(rq, (qr * D + 32 * kk + 8 * g) * 2));
+      of[qs][kk] = as_bf16x8(bload16(ro, (qr * D + 32 * kk + 8 * g) * 2));
+    }
+    lse2[qs] = INFINITY;
+    Dq[qs] = 0.f;
+    if (qr < c) {
+      const float lv = a.lse[so + qr];
+      lse2[qs] = (lv == -INFINITY) ? INFINITY : lv * kBwdLog2e;
+      Dq[qs] = a.D[so + qr];
+    }
   }
-  float lse2 = INFINITY, Dq = 0.f;
-  if (row_ok) {
-    const float lv = a.lse[so + qr];
-    lse2 = (lv == -INFINITY) ? INFINITY : lv * kBwdLog2e;
-    Dq = a.D[so + qr];
-  }
-  f32x16 acc[NDT];
+  // dQ^T accumulators: d tile nt, sub-tile qs; value r of lane (g, i) is
+  // d 16nt + 4g + r of row qw0 + 16qs + i.
+  f32x4 acc[NT][2];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[nt][qs][r] = 0.f;
+
+  // Loop-invariant LDS offsets: row reads of row 16mt + i, global chunk
+  // 4kk + g; transposing reads of d tile nt (see STile::tr16_off).
+  int roff[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) roff[kk] = l16 * T::ROWB + (((4 * kk + g) ^ tile::swz<D, tile::kSwz16>(l16)) * 16);
+  int toff[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) toff[nt] = T::tr16_off(16 * nt, lane);
 
   const float c2 = a.scale_log2;
+  // One 64-key tile (4 MFMA row tiles mt of 16 keys) against this wave's 32
+  // rows, with v_mfma_f32_16x16x32_bf16:
+  //  A  S^T = K Q^T, dP^T = V dO^T: slot u = (mt, kk) reads one K row and one
+  //     V row operand and feeds four MFMAs (both row sub-tiles); keys
+  //     16mt + 4g + r of a tile land in value r of lane (g, i);
+  //  B  dS^T = P^T (dP^T - D), P = 2^(S c2 - lse2), per half of the keys;
+  //  C  dQ^T += K^T dS^T over key steps kq (32 keys = half kq): slot
+  //     v = (kq, nt) reads the transposed K operand and feeds two MFMAs.
+  //     dS^T's item j of lane (g, i) is key 32kq + 16(j/4) + 4g + j%4, the
+  //     order in which the transposing read delivers K.
   auto step = [&](int t, auto masked) {
     if (t + 1 < ntiles) {
       unsigned char* nb = smem + ((t + 1) & 1) * BUF;
@@ -412,45 +471,71 @@ void dq_kernel(BwdArgs a) {
       T::dma(rv, nb + T::BYTES, (t + 1) * kTile, wave, lane);
     }
     const int kb0 = t * kTile;
-    const unsigned char* ks = smem + (t & 1) * BUF;
-    const unsigned char* vs = ks + T::BYTES;
-    f32x16 s[2], dpv[2];
+    const unsigned char* ks_ = smem + (t & 1) * BUF;
+    const unsigned char* vs_ = ks_ + T::BYTES;
+    constexpr int NU = 2 * NKK, NC = 2 * NT, kPre = 2;     // slots per half (A), per tile (C)
+    bf16x8 dsb[2][2];                                      // [qs][kq]
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x4 s[2][2], dpv[2][2];                            // [mt - 2hf][qs]
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[mt][r] = 0.f;
-        dpv[mt][r] = 0.f;
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            s[m][qs][r] = 0.f;
+            dpv[m][qs][r] = 0.f;
+          }
+      bf16x8 ka[NU], va[NU];
+      auto a_read = [&](int u) {
+        const int mt = 2 * hf + u / NKK, kk = u % NKK;
+        ka[u] = *reinterpret_cast<const bf16x8*>(ks_ + 16 * mt * T::ROWB + roff[kk]);
+        va[u] = *reinterpret_cast<const bf16x8*>(vs_ + 16 * mt * T::ROWB + roff[kk]);
+      };
+#pragma unroll
+      for (int u = 0; u < kPre; ++u) a_read(u);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        if (u + kPre < NU) a_read(u + kPre);
+        const int m = u / NKK, kk = u % NKK;
+        s[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u], qf[0][kk], s[m][0], 0, 0, 0);
+        s[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u], qf[1][kk], s[m][1], 0, 0, 0);
+        dpv[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u], of[0][kk], dpv[m][0], 0, 0, 0);
+        dpv[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[u], of[1][kk], dpv[m][1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);                 // keep the reads kPre slots ahead
       }
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::row(ks, 32 * mt + l32, 2 * kk + hh), qf[kk], s[mt], 0, 0, 0);
-        dpv[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::row(vs, 32 * mt + l32, 2 * kk + hh), of[kk], dpv[mt], 0, 0, 0);
-      }
+        for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+          for (int r = 0; r < 4; ++r) {
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[m][qs][r], c2, -lse2[qs]));
+            if constexpr (decltype(masked)::value) {
+              const int kr = kb0 + 16 * (2 * hf + m) + 4 * g + r;
+              const int qr = qw0 + 16 * qs + l16;
+              const bool vis = (kr < c) & visible(kr - qr, delta);
+              p = vis ? p : 0.f;
+            }
+            dsb[qs][hf][4 * m + r] = (__bf16)(p * (dpv[m][qs][r] - Dq[qs]));
+          }
+    }
+    bf16x8 kt[NC];
+    auto c_read = [&](int v) {
+      const int kq = v / NT, nt = v % NT;
+      kt[v] = T::tr_at(ks_ + 32 * kq * T::ROWB, toff[nt], toff[nt] + 16 * T::ROWB);
+    };
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float sv = s[mt][r];
-        if constexpr (decltype(masked)::value) {
-          const int kr = kb0 + 32 * mt + (r >> 2) * 8 + 4 * hh + (r & 3);
-          if (!(kr < c && visible(kr - qr, delta))) sv = -INFINITY;
-        }
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c2, -lse2));
-        dpv[mt][r] = p * (dpv[mt][r] - Dq);
-      }
-    bf16x8 dsb[4];
+    for (int v = 0; v < kPre; ++v) c_read(v);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) dsb[kk][j] = (__bf16)dpv[kk >> 1][8 * (kk & 1) + j];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T::tr(ks, 16 * kk, 32 * dt, lane), dsb[kk], acc[dt], 0, 0, 0);
+    for (int v = 0; v < NC; ++v) {
+      if (v + kPre < NC) c_read(v + kPre);
+      const int kq = v / NT, nt = v % NT;
+      acc[nt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt[v], dsb[0][kq], acc[nt][0], 0, 0, 0);
+      acc[nt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt[v], dsb[1][kq], acc[nt][1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     dma_wait();
     __syncthreads();
   };
@@ -464,21 +549,23 @@ void dq_kernel(BwdArgs a) {
   for (int t = 0; t < n_unmasked; ++t) step(t, std::false_type{});
   for (int t = n_unmasked; t < ntiles; ++t) step(t, std::true_type{});
 
-  if (row_ok) {
-    const float scale = a.scale;
+  const float scale = a.scale;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+  for (int qs = 0; qs < 2; ++qs) {
+    const int qr = qw0 + 16 * qs + l16;
+    if (qr < c) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float* p = dqp + (int64_t)qr * D + 32 * dt + 8 * g + 4 * hh;
-        float4 v = make_float4(scale * acc[dt][4 * g + 0], scale * acc[dt][4 * g + 1],
-                               scale * acc[dt][4 * g + 2], scale * acc[dt][4 * g + 3]);
+      for (int nt = 0; nt < NT; ++nt) {
+        float* p = dqp + (int64_t)qr * D + 16 * nt + 4 * g;
+        float4 v = make_float4(scale * acc[nt][qs][0], scale * acc[nt][qs][1], scale * acc[nt][qs][2],
+                               scale * acc[nt][qs][3]);
         if (a.dq_accumulate) {
           const float4 o = *reinterpret_cast<const float4*>(p);
           v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
         }
         *reinterpret_cast<float4*>(p) = v;
       }
+    }
   }
 }
 

@@ -47,6 +47,7 @@ namespace ra {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBN = 64;        // keys per tile
 constexpr int kThreads = 256;  // 4 waves
@@ -80,12 +81,13 @@ struct FwdTile {
 template <int D, int HPW>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(RA_FWD_WAVES, RA_FWD_WAVES)))
 void fwd_bf16_kernel(FwdArgs a) {
-  using T = FwdTile<D>;
+  using S = tile::STile<D, tile::kSwz16>;
   constexpr int WPH = 4 / HPW;          // waves per head
   constexpr int ROWS = 32 * WPH;        // query rows per workgroup
-  constexpr int NDT = D / 32;           // 32-wide d tiles of O^T
-  constexpr int NKK = D / 16;           // 16-deep steps of the score MFMA
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[T::BYTES];
+  constexpr int NKK = D / 32;           // 32-deep d steps of the score MFMA
+  constexpr int NT = D / 16;            // 16-row d tiles of O^T
+  constexpr int TILE = S::BYTES;        // bytes per 64-key tile
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILE];   // K[2], V[2]
 
   const int c = a.c;
   const int n_rt = (c + ROWS - 1) / ROWS;
@@ -110,14 +112,10 @@ void fwd_bf16_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;                        // lane half
+  const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
   const int head = hg * HPW + wave / WPH;
   const int kvh = head / (a.hq / a.hkv);
-  const int qw0 = q0 + (wave % WPH) * 32;          // first row of this wave
-  const int qr = qw0 + l32;                        // this lane's query row
-  const bool row_ok = qr < c;
+  const int qw0 = q0 + (wave % WPH) * 32;          // this wave's rows: sub-tiles of 16
 
   const int blk_bytes = c * D * 2;
   const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + host * a.q_host_stride +
@@ -133,177 +131,196 @@ void fwd_bf16_kernel(FwdArgs a) {
   float* lp = a.l + host * a.ml_host_stride + (int64_t)(b * a.hq + head) * c;
   float* op = a.o + host * a.q_host_stride + ((int64_t)(b * a.hq + head) * c) * D;
 
-  // ---- Q fragments (B operand of S^T = K Q^T): d = 16kk + 8hh + j ----
-  bf16x8 qf[NKK];
+  // ---- Q^T fragments (B operand of S^T = K Q^T): sub-tile qs, d step kk,
+  // lane (g, i) holds d 32kk + 8g .. +7 of row qw0 + 16qs + i ----
+  bf16x8 qf[2][NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) qf[kk] = as_bf16x8(bload16(rq, (qr * D + 16 * kk + 8 * hh) * 2));
-
-  // ---- state: reference max m_ref (base 2), true max, per-half partial l, O^T ----
-  float m_ref = -INFINITY, lh = 0.f;
-  f32x16 acc_o[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc_o[dt][r] = 0.f;
-  if (row_ok) {
-    m_ref = mp[qr] * kLog2e;          // -inf stays -inf
-    lh = (hh == 0) ? lp[qr] : 0.f;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 v = *reinterpret_cast<const float4*>(op + (int64_t)qr * D + 32 * dt + 8 * g + 4 * hh);
-        acc_o[dt][4 * g + 0] = v.x;
-        acc_o[dt][4 * g + 1] = v.y;
-        acc_o[dt][4 * g + 2] = v.z;
-        acc_o[dt][4 * g + 3] = v.w;
-      }
-  }
-  float m_true = m_ref;
-
-  // ---- LDS-DMA tile loads and per-lane LDS read offsets ----
-  using S = typename T::S;
-  auto dma_k = [&](int t, int buf) { S::dma(rk, smem + buf * T::TILE, t * kBN, wave, lane); };
-  auto dma_v = [&](int t, int buf) { S::dma(rv, smem + (2 + buf) * T::TILE, t * kBN, wave, lane); };
-  // scores: A operand row R = 32mt + l32 (swizzle depends on R % 16 only),
-  // global chunk 2kk + hh
-  const int ksw = tile::swz<D>(l32);
-  // P V: transposing reads over rows 16kk.. of the V tile; the swizzle depends
-  // on the row mod 16, so the offsets for kk = 0 serve every kk
-  int v_lo[NDT], v_hi[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    v_lo[dt] = S::tr_off(0, 32 * dt, lane);
-    v_hi[dt] = S::tr_off(8, 32 * dt, lane);
-  }
-
-  auto scores = [&](int buf, f32x16 (&s)[2]) {
-    const unsigned char* ks = smem + buf * T::TILE;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
+  for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
+      qf[qs][kk] = as_bf16x8(bload16(rq, ((qw0 + 16 * qs + l16) * D + 32 * kk + 8 * g) * 2));
+
+  // ---- state per sub-tile: reference max m_ref (base 2), true max, this
+  // lane's partial l (lane group g == 0 carries the stored l), O^T with
+  // value r of lane (g, i) = d 16nt + 4g + r of row qw0 + 16qs + i ----
+  float m_ref[2], m_true[2], lh[2];
+  f32x4 acc_o[NT][2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int R = 32 * mt + l32;
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(ks + R * S::ROWB + (((2 * kk + hh) ^ ksw) * 16));
-        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[mt], 0, 0, 0);
+  for (int qs = 0; qs < 2; ++qs) {
+    const int qr = qw0 + 16 * qs + l16;
+    m_ref[qs] = -INFINITY;
+    lh[qs] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc_o[nt][qs][r] = 0.f;
+    if (qr < c) {
+      m_ref[qs] = mp[qr] * kLog2e;          // -inf stays -inf
+      lh[qs] = (g == 0) ? lp[qr] : 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float4 v = *reinterpret_cast<const float4*>(op + (int64_t)qr * D + 16 * nt + 4 * g);
+        acc_o[nt][qs][0] = v.x;
+        acc_o[nt][qs][1] = v.y;
+        acc_o[nt][qs][2] = v.z;
+        acc_o[nt][qs][3] = v.w;
       }
-  };
-  auto pv = [&](int buf, const bf16x8 (&pb)[4]) {
-    const unsigned char* vs = smem + (2 + buf) * T::TILE;
+    }
+    m_true[qs] = m_ref[qs];
+  }
+
+  // ---- LDS-DMA tile loads and loop-invariant LDS offsets ----
+  auto dma_k = [&](int t, int buf) { S::dma(rk, smem + buf * TILE, t * kBN, wave, lane); };
+  auto dma_v = [&](int t, int buf) { S::dma(rv, smem + (2 + buf) * TILE, t * kBN, wave, lane); };
+  // row reads of K: row 16mt + i, global chunk 4kk + g
+  int roff[NKK];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+  for (int kk = 0; kk < NKK; ++kk) roff[kk] = l16 * S::ROWB + (((4 * kk + g) ^ tile::swz<D, tile::kSwz16>(l16)) * 16);
+  // transposing reads of V: d tile nt (see STile::tr16_off)
+  int toff[NT];
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const bf16x8 va = S::tr_at(vs + (16 * kk) * S::ROWB, v_lo[dt], v_hi[dt]);
-        acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kk], acc_o[dt], 0, 0, 0);
-      }
-  };
-  // masked row max of a score tile (base-2 units, combined over the two lane halves)
+  for (int nt = 0; nt < NT; ++nt) toff[nt] = S::tr16_off(16 * nt, lane);
+
   const float c2 = a.scale_log2;
-  auto tile_max = [&](f32x16 (&s)[2], int k0, auto masked_tag) -> float {
-    if constexpr (decltype(masked_tag)::value) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * mt + (r >> 2) * 8 + 4 * hh + (r & 3);
-          if (!(key < c && visible(key - qr, delta))) s[mt][r] = -INFINITY;
-        }
-    }
-    float mx = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[0][r], s[0][r + 1]));
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[1][r], s[1][r + 1]));
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c2;
+  // row max / row sum across the four 16-lane groups of a row
+  auto allmax = [](float x) {
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
   };
-  // move the reference max (rescaling O and l) only when some row's max grew
-  // past the threshold
-  auto rescale = [&](float mx) {
-    m_true = fmaxf(m_true, mx);
-    if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleThreshold)) {
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_ref - m_new);
-      lh *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
-      m_ref = m_new;
-    }
-  };
-  // P = 2^(S c2 - m_ref) as bf16 fragments: the 16-key step kk takes values
-  // 8(kk%2)..+7 of the 32-key half kk/2, i.e. keys 16kk + 8(j/4) + 4hh + j%4
-  auto exp_pack = [&](const f32x16 (&s)[2], bf16x8 (&pb)[4]) {
-    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-    float rs = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kk >> 1][8 * (kk & 1) + j], c2, -m_use));
-        rs += p;
-        pb[kk][j] = (__bf16)p;
-      }
-    lh += rs;
+  auto allsum = [](float x) {
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
   };
 
-  // ---- tile loop: iteration t computes and folds tile t; the DMA of tile
-  // t+1 into the other K/V buffers (last read in iteration t-1) overlaps it.
-  dma_k(0, 0);
-  dma_v(0, 0);
-  tile::dma_wait();
-  __syncthreads();
+  // ---- one 64-key tile (4 MFMA row tiles mt of 16 keys), v_mfma_f32_16x16x32_bf16:
+  //  S^T = K Q^T: slot u = (mt, kk) reads one K row operand, feeds both
+  //  sub-tiles; key 16mt + 4g + r of the tile is value r of lane (g, i).
+  //  O^T += V^T P^T over key steps kq (32 keys): slot v = (kq, nt) reads the
+  //  transposed V operand; P^T's item j of lane (g, i) is key 32kq + 16(j/4)
+  //  + 4g + j%4, the order in which the transposing read delivers V.
   auto step = [&](int t, auto masked) {
     if (t + 1 < ntiles) {
       dma_k(t + 1, (t + 1) & 1);
       dma_v(t + 1, (t + 1) & 1);
     }
-    f32x16 s[2];
-    scores(t & 1, s);
-    const float mx = tile_max(s, t * kBN, masked);
-    rescale(mx);
-    bf16x8 pb[4];
-    exp_pack(s, pb);
-    pv(t & 1, pb);
-    // P V MFMAs with their transposing V reads running 2 MFMAs ahead
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    const unsigned char* ks = smem + (t & 1) * TILE;
+    const unsigned char* vs = smem + (2 + (t & 1)) * TILE;
+    const int kb0 = t * kBN;
+    constexpr int NU = 4 * NKK, NC = 2 * NT, kPre = 2;
+    f32x4 s[4][2];
 #pragma unroll
-    for (int i = 0; i < 4 * NDT; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[mt][qs][r] = 0.f;
+    bf16x8 ka[NU], vt[NC];
+    auto a_read = [&](int u) {
+      ka[u] = *reinterpret_cast<const bf16x8*>(ks + 16 * (u / NKK) * S::ROWB + roff[u % NKK]);
+    };
+    auto c_read = [&](int v) {
+      const int kq = v / NT, nt = v % NT;
+      vt[v] = S::tr_at(vs + 32 * kq * S::ROWB, toff[nt], toff[nt] + 16 * S::ROWB);
+    };
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) a_read(u);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      if (u + kPre < NU) a_read(u + kPre);
+      else c_read(u + kPre - NU);
+      const int mt = u / NKK, kk = u % NKK;
+      s[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u], qf[0][kk], s[mt][0], 0, 0, 0);
+      s[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u], qf[1][kk], s[mt][1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);                   // keep the reads kPre slots ahead
+    }
+    // online softmax per sub-tile: masked row max, lazy rescale, P
+    bf16x8 pb[2][2];                                       // [kq][qs]
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      if constexpr (decltype(masked)::value) {
+        const int qr = qw0 + 16 * qs + l16;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = kb0 + 16 * mt + 4 * g + r;
+            const bool vis = (key < c) & visible(key - qr, delta);
+            s[mt][qs][r] = vis ? s[mt][qs][r] : -INFINITY;
+          }
+      }
+      float mx = fmaxf(fmaxf(s[0][qs][0], s[0][qs][1]), fmaxf(s[0][qs][2], s[0][qs][3]));
+#pragma unroll
+      for (int mt = 1; mt < 4; ++mt)
+        mx = fmaxf(mx, fmaxf(fmaxf(s[mt][qs][0], s[mt][qs][1]), fmaxf(s[mt][qs][2], s[mt][qs][3])));
+      mx = allmax(mx) * c2;
+      m_true[qs] = fmaxf(m_true[qs], mx);
+      // move the reference max (rescaling O and l) only when some row's max
+      // grew past the threshold
+      if (__builtin_amdgcn_ballot_w64(mx > m_ref[qs] + kRescaleThreshold)) {
+        const float m_new = fmaxf(m_ref[qs], mx);
+        const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_ref[qs] - m_new);
+        lh[qs] *= alpha;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc_o[nt][qs][r] *= alpha;
+        m_ref[qs] = m_new;
+      }
+      const float m_use = (m_ref[qs] == -INFINITY) ? 0.f : m_ref[qs];
+      float rs = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][qs][r], c2, -m_use));
+          rs += p;
+          pb[mt >> 1][qs][4 * (mt & 1) + r] = (__bf16)p;
+        }
+      lh[qs] += rs;
+    }
+#pragma unroll
+    for (int v = 0; v < NC; ++v) {
+      if (v + kPre < NC) c_read(v + kPre);
+      const int kq = v / NT, nt = v % NT;
+      acc_o[nt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[v], pb[kq][0], acc_o[nt][0], 0, 0, 0);
+      acc_o[nt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[v], pb[kq][1], acc_o[nt][1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     tile::dma_wait();
     __syncthreads();
   };
+  dma_k(0, 0);
+  dma_v(0, 0);
+  tile::dma_wait();
+  __syncthreads();
   for (int t = 0; t < n_unmasked; ++t) step(t, std::false_type{});
   for (int t = n_unmasked; t < ntiles; ++t) step(t, std::true_type{});
 
   // ---- write the state back, referenced to the true running max ----
-  const float fix = (m_true == -INFINITY || m_ref == m_true) ? 1.f : exp2f(m_ref - m_true);
-  lh *= fix;
-  const float l_tot = lh + __shfl_xor(lh, 32);
-  if (row_ok) {
-    if (hh == 0) {
-      mp[qr] = m_true * kLn2;
-      lp[qr] = l_tot;
-    }
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float4 v;
-        v.x = acc_o[dt][4 * g + 0] * fix;
-        v.y = acc_o[dt][4 * g + 1] * fix;
-        v.z = acc_o[dt][4 * g + 2] * fix;
-        v.w = acc_o[dt][4 * g + 3] * fix;
-        *reinterpret_cast<float4*>(op + (int64_t)qr * D + 32 * dt + 8 * g + 4 * hh) = v;
+  for (int qs = 0; qs < 2; ++qs) {
+    const float fix = (m_true[qs] == -INFINITY || m_ref[qs] == m_true[qs]) ? 1.f : exp2f(m_ref[qs] - m_true[qs]);
+    const float l_tot = allsum(lh[qs] * fix);
+    const int qr = qw0 + 16 * qs + l16;
+    if (qr < c) {
+      if (g == 0) {
+        mp[qr] = m_true[qs] * kLn2;
+        lp[qr] = l_tot;
       }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float4 v;
+        v.x = acc_o[nt][qs][0] * fix;
+        v.y = acc_o[nt][qs][1] * fix;
+        v.z = acc_o[nt][qs][2] * fix;
+        v.w = acc_o[nt][qs][3] * fix;
+        *reinterpret_cast<float4*>(op + (int64_t)qr * D + 16 * nt + 4 * g) = v;
+      }
+    }
   }
 }
 

@@ -38,20 +38,26 @@ __device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" :
 // A tile of kRows rows x D bf16 lives in LDS row-major, unpadded (2*D bytes
 // per row); LDS chunk C (16 bytes) of row R holds global chunk C ^ swz(R).
 // LDS serves 256 bytes per clock over 64 banks: a 16-byte read is served 16
-// lanes at a time and an 8-byte read 32 lanes at a time.  The swizzle keeps
-// both read patterns below conflict-free:
-//  * row reads (MFMA operand with one row per lane): 16 consecutive rows, one
-//    chunk each, must fall on 16 distinct 16-byte bank groups;
-//  * transposing reads (ds_read_b64_tr_b16): 32 lanes cover 4 consecutive
-//    rows (aligned to 4) x 4 consecutive chunks (aligned to 4), which must
-//    again fall on 16 distinct bank groups.
-// d = 128 (16 chunks, 256-byte rows): swz(R) = 4 (R % 4) + (R / 4) % 4.
-// d = 64 (8 chunks, 128-byte rows, two rows per 256 bytes):
-//   swz(R) = 4 ((R / 2) % 2) + (R / 4) % 4.
-template <int D>
+// lanes at a time and an 8-byte read 32 lanes at a time.  Row reads (MFMA
+// operand, one row per lane) put 16 consecutive rows, one chunk each, in a
+// pass; the transposing reads (ds_read_b64_tr_b16) put either 4 consecutive
+// rows x 4 consecutive chunks (operands of the 32x32x16 MFMA: kSwz32) or
+// 8 consecutive rows x 2 consecutive chunks (16x16x32 MFMA: kSwz16) in a
+// pass.  Each swizzle maps both of its patterns onto 16 distinct 16-byte bank
+// groups (conflict-free), and depends on the row mod 16 only.
+//  kSwz32, d = 128: 4 (R % 4) + (R / 4) % 4;  d = 64: 4 ((R / 2) % 2) + (R / 4) % 4
+//  kSwz16, d = 128: 2 (R % 8) + (R / 8) % 2;  d = 64: 2 ((R / 2) % 4) + (R / 8) % 2
+// (for d = 64 two rows share a 256-byte bank line).
+constexpr int kSwz32 = 0, kSwz16 = 1;
+template <int D, int V = kSwz32>
 __device__ inline int swz(int R) {
-  if constexpr (D == 128) return 4 * (R & 3) + ((R >> 2) & 3);
-  else return 4 * ((R >> 1) & 1) + ((R >> 2) & 3);
+  if constexpr (V == kSwz32) {
+    if constexpr (D == 128) return 4 * (R & 3) + ((R >> 2) & 3);
+    else return 4 * ((R >> 1) & 1) + ((R >> 2) & 3);
+  } else {
+    if constexpr (D == 128) return 2 * (R & 7) + ((R >> 3) & 1);
+    else return 2 * ((R >> 1) & 3) + ((R >> 3) & 1);
+  }
 }
 
 // LDS reads and LDS-DMA: the compiler orders an LDS read that carries no
@@ -67,7 +73,7 @@ __device__ __forceinline__ i16x4 tr_read(__attribute__((address_space(3))) i16x4
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
 }
 
-template <int D>
+template <int D, int V = kSwz32>
 struct STile {
   static constexpr int ROWB = 2 * D;
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
@@ -85,12 +91,12 @@ struct STile {
       const int ins = wave * DPW + i;
       const int R = ins * RPI + lane / CPR;
       const int C = lane % CPR;
-      dma16(r, lds + ins * 1024, (row0 + R) * ROWB + ((C ^ swz<D>(R)) * 16));
+      dma16(r, lds + ins * 1024, (row0 + R) * ROWB + ((C ^ swz<D, V>(R)) * 16));
     }
   }
   // 16-byte row read: global chunk c of row R.
   __device__ static bf16x8 row(const unsigned char* lds, int R, int c) {
-    return *reinterpret_cast<const bf16x8*>(lds + R * ROWB + ((c ^ swz<D>(R)) * 16));
+    return *reinterpret_cast<const bf16x8*>(lds + R * ROWB + ((c ^ swz<D, V>(R)) * 16));
   }
   // Transposed MFMA operand over 16 tile rows starting at rbase (a multiple
   // of 16): lane (G = lane / 16, j = lane % 16) gets column dcol0 + 16 (G % 2)
@@ -108,13 +114,25 @@ struct STile {
     const int a = jj & 3, k = jj >> 2, h = G >> 1, dh = G & 1;
     const int chunk = (dcol0 + 16 * dh + 4 * a) / 8;
     const int r = half8 + 4 * h + k;
-    return r * ROWB + ((chunk ^ swz<D>(r)) * 16) + 8 * (a & 1);
+    return r * ROWB + ((chunk ^ swz<D, V>(r)) * 16) + 8 * (a & 1);
   }
   __device__ static bf16x8 tr_at(const unsigned char* lds, int off_lo, int off_hi) {
     const i16x4 lo = tr_read((__attribute__((address_space(3))) i16x4*)(lds + off_lo));
     const i16x4 hi = tr_read((__attribute__((address_space(3))) i16x4*)(lds + off_hi));
     const i16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8, w);
+  }
+  // 16x16x32 operand over tile rows rbase + (0..31) (rbase a multiple of 16):
+  // lane (g = lane / 16, i = lane % 16) gets column dcol0 + i of rows
+  // rbase + 4g + 0..3 (items 0..3) and rbase + 16 + 4g + 0..3 (items 4..7).
+  // In each 16-lane group lane i addresses row rbase + 4g + i/4 at columns
+  // dcol0 + 4 (i % 4) .. +3.  tr16_off gives the offset for rbase = 0; the
+  // items 4..7 read is the same offset + 16 rows (the swizzle has period 16).
+  __device__ static int tr16_off(int dcol0, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const int r = 4 * g + (i >> 2);
+    const int col = dcol0 + 4 * (i & 3);
+    return r * ROWB + (((col >> 3) ^ swz<D, V>(r)) * 16) + 8 * ((col >> 2) & 1);
   }
   __device__ static bf16x8 tr(const unsigned char* lds, int rbase, int dcol0, int lane) {
     return tr_at(lds + rbase * ROWB, tr_off(0, dcol0, lane), tr_off(8, dcol0, lane));
