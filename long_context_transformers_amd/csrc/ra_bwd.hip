@@ -369,7 +369,8 @@ void dkdv_kernel(BwdArgs a) {
 template <int D, int HPW>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(RA_DQ_WAVES, RA_DQ_WAVES)))
 void dq_kernel(BwdArgs a) {
-  using T = tile::STile<D, tile::kSwz16>;
+  using T = tile::STile<D, tile::kSwz16>;                  // K: row and transposing reads
+  using TV = tile::STile<D, tile::kSwzRow>;                // V: row reads only
   constexpr int WPH = 4 / HPW;
   constexpr int ROWS = 32 * WPH;
   constexpr int NKK = D / 32;                              // 32-deep d steps of S^T, dP^T
@@ -446,9 +447,12 @@ void dq_kernel(BwdArgs a) {
 
   // Loop-invariant LDS offsets: row reads of row 16mt + i, global chunk
   // 4kk + g; transposing reads of d tile nt (see STile::tr16_off).
-  int roff[NKK];
+  int roff[NKK], rvoff[NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) roff[kk] = l16 * T::ROWB + (((4 * kk + g) ^ tile::swz<D, tile::kSwz16>(l16)) * 16);
+  for (int kk = 0; kk < NKK; ++kk) {
+    roff[kk] = l16 * T::ROWB + (((4 * kk + g) ^ tile::swz<D, tile::kSwz16>(l16)) * 16);
+    rvoff[kk] = l16 * T::ROWB + (((4 * kk + g) ^ tile::swz<D, tile::kSwzRow>(l16)) * 16);
+  }
   int toff[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) toff[nt] = T::tr16_off(16 * nt, lane);
@@ -468,7 +472,7 @@ void dq_kernel(BwdArgs a) {
     if (t + 1 < ntiles) {
       unsigned char* nb = smem + ((t + 1) & 1) * BUF;
       T::dma(rk, nb, (t + 1) * kTile, wave, lane);
-      T::dma(rv, nb + T::BYTES, (t + 1) * kTile, wave, lane);
+      TV::dma(rv, nb + T::BYTES, (t + 1) * kTile, wave, lane);
     }
     const int kb0 = t * kTile;
     const unsigned char* ks_ = smem + (t & 1) * BUF;
@@ -491,7 +495,7 @@ void dq_kernel(BwdArgs a) {
       auto a_read = [&](int u) {
         const int mt = 2 * hf + u / NKK, kk = u % NKK;
         ka[u] = *reinterpret_cast<const bf16x8*>(ks_ + 16 * mt * T::ROWB + roff[kk]);
-        va[u] = *reinterpret_cast<const bf16x8*>(vs_ + 16 * mt * T::ROWB + roff[kk]);
+        va[u] = *reinterpret_cast<const bf16x8*>(vs_ + 16 * mt * T::ROWB + rvoff[kk]);
       };
 #pragma unroll
       for (int u = 0; u < kPre; ++u) a_read(u);
@@ -542,7 +546,7 @@ void dq_kernel(BwdArgs a) {
 
   if (ntiles > 0) {
     T::dma(rk, smem, 0, wave, lane);
-    T::dma(rv, smem + T::BYTES, 0, wave, lane);
+    TV::dma(rv, smem + T::BYTES, 0, wave, lane);
     dma_wait();
   }
   __syncthreads();

@@ -81,7 +81,8 @@ struct FwdTile {
 template <int D, int HPW>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(RA_FWD_WAVES, RA_FWD_WAVES)))
 void fwd_bf16_kernel(FwdArgs a) {
-  using S = tile::STile<D, tile::kSwz16>;
+  using S = tile::STile<D, tile::kSwz16>;     // V: transposing reads
+  using SK = tile::STile<D, tile::kSwzRow>;   // K: row reads
   constexpr int WPH = 4 / HPW;          // waves per head
   constexpr int ROWS = 32 * WPH;        // query rows per workgroup
   constexpr int NKK = D / 32;           // 32-deep d steps of the score MFMA
@@ -170,12 +171,12 @@ void fwd_bf16_kernel(FwdArgs a) {
   }
 
   // ---- LDS-DMA tile loads and loop-invariant LDS offsets ----
-  auto dma_k = [&](int t, int buf) { S::dma(rk, smem + buf * TILE, t * kBN, wave, lane); };
+  auto dma_k = [&](int t, int buf) { SK::dma(rk, smem + buf * TILE, t * kBN, wave, lane); };
   auto dma_v = [&](int t, int buf) { S::dma(rv, smem + (2 + buf) * TILE, t * kBN, wave, lane); };
   // row reads of K: row 16mt + i, global chunk 4kk + g
   int roff[NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) roff[kk] = l16 * S::ROWB + (((4 * kk + g) ^ tile::swz<D, tile::kSwz16>(l16)) * 16);
+  for (int kk = 0; kk < NKK; ++kk) roff[kk] = l16 * S::ROWB + (((4 * kk + g) ^ tile::swz<D, tile::kSwzRow>(l16)) * 16);
   // transposing reads of V: d tile nt (see STile::tr16_off)
   int toff[NT];
 #pragma unroll

@@ -37,26 +37,33 @@ __device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" :
 
 // A tile of kRows rows x D bf16 lives in LDS row-major, unpadded (2*D bytes
 // per row); LDS chunk C (16 bytes) of row R holds global chunk C ^ swz(R).
-// LDS serves 256 bytes per clock over 64 banks: a 16-byte read is served 16
-// lanes at a time and an 8-byte read 32 lanes at a time.  Row reads (MFMA
-// operand, one row per lane) put 16 consecutive rows, one chunk each, in a
-// pass; the transposing reads (ds_read_b64_tr_b16) put either 4 consecutive
-// rows x 4 consecutive chunks (operands of the 32x32x16 MFMA: kSwz32) or
-// 8 consecutive rows x 2 consecutive chunks (16x16x32 MFMA: kSwz16) in a
-// pass.  Each swizzle maps both of its patterns onto 16 distinct 16-byte bank
-// groups (conflict-free), and depends on the row mod 16 only.
-//  kSwz32, d = 128: 4 (R % 4) + (R / 4) % 4;  d = 64: 4 ((R / 2) % 2) + (R / 4) % 4
-//  kSwz16, d = 128: 2 (R % 8) + (R / 8) % 2;  d = 64: 2 ((R / 2) % 4) + (R / 8) % 2
+// The swizzle is chosen per tile for the reads that tile sees:
+//  * row reads (MFMA operand with one row per lane; a 16x16x32 operand puts
+//    16 consecutive rows of one chunk in a 16-lane group);
+//  * transposing reads (ds_read_b64_tr_b16): a 32x32x16 operand covers 4 rows
+//    x 4 chunks per 32 lanes, a 16x16x32 operand 8 rows x 2 chunks.
+// Measured on gfx950 (SQ_LDS_BANK_CONFLICT per instruction, d = 128): the
+// 16x16x32 row reads are conflict-free iff the swizzle's bit 0 comes from
+// row bit 0 or 1, the 16x16x32 transposing reads iff it comes from row bit 3
+// (within 8 rows the chunk parity must be kept); no single swizzle serves both,
+// so a tile read both ways uses kSwz16 (transposing reads clean, row reads
+// 4 extra cycles each) and a tile read only by rows uses kSwzRow.
+//  kSwz32,  d = 128: 4 (R % 4) + (R / 4) % 4;  d = 64: 4 ((R / 2) % 2) + (R / 4) % 4
+//  kSwz16,  d = 128: 2 (R % 8) + (R / 8) % 2;  d = 64: 2 ((R / 2) % 4) + (R / 8) % 2
+//  kSwzRow, d = 128: R % 16;                   d = 64: (R / 2) % 8
 // (for d = 64 two rows share a 256-byte bank line).
-constexpr int kSwz32 = 0, kSwz16 = 1;
+constexpr int kSwz32 = 0, kSwz16 = 1, kSwzRow = 2;
 template <int D, int V = kSwz32>
 __device__ inline int swz(int R) {
   if constexpr (V == kSwz32) {
     if constexpr (D == 128) return 4 * (R & 3) + ((R >> 2) & 3);
     else return 4 * ((R >> 1) & 1) + ((R >> 2) & 3);
-  } else {
+  } else if constexpr (V == kSwz16) {
     if constexpr (D == 128) return 2 * (R & 7) + ((R >> 3) & 1);
     else return 2 * ((R >> 1) & 3) + ((R >> 3) & 1);
+  } else {
+    if constexpr (D == 128) return R & 15;
+    else return (R >> 1) & 7;
   }
 }
 
