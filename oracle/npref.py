@@ -33,14 +33,21 @@ import numpy as np
 
 LAYOUT_CONTIGUOUS = 0
 LAYOUT_STRIPED = 1
+LAYOUT_ZIGZAG = 2
 
 
 def token_index(layout: int, n_hosts: int, block_len: int, host, r):
-    """Global token of local row r on host ``host``."""
+    """Global token of local row r on host ``host``.  Zigzag (named, not
+    defined, in P1 "工程实践指南" as the causal load-balancing variant beside
+    Striped; reading used here): 2N chunks of c/2 tokens, host h holds chunk h
+    in rows 0..c/2-1 and chunk 2N-1-h in rows c/2..c-1."""
     host = np.asarray(host, dtype=np.int64)
     r = np.asarray(r, dtype=np.int64)
     if layout == LAYOUT_STRIPED:
         return r * n_hosts + host
+    if layout == LAYOUT_ZIGZAG:
+        half = block_len // 2
+        return np.where(r < half, host * half + r, (2 * n_hosts - 1 - host) * half + (r - half))
     return host * block_len + r
 
 

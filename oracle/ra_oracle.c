@@ -43,13 +43,25 @@
 
 #define OR_LAYOUT_CONTIGUOUS 0
 #define OR_LAYOUT_STRIPED 1
+#define OR_LAYOUT_ZIGZAG 2
 
-/* Global token index of local row r on host h. */
+/* Global token index of local row r on host h.
+ * Contiguous: host h holds tokens [h c, (h+1) c).  Striped: token r N + h.
+ * Zigzag (named beside Striped as the causal load-balancing variant in P1,
+ * "工程实践指南", item "因果掩码"; the pages give no definition, the reading
+ * used here): the sequence is cut into 2N chunks of c/2 tokens and host h
+ * holds chunk h (its rows 0..c/2-1) and chunk 2N-1-h (rows c/2..c-1). */
 static inline long long token_index(int layout, int n_hosts, long long block_len, int host,
                                     long long r)
 {
     if (layout == OR_LAYOUT_STRIPED)
         return r * (long long)n_hosts + host;
+    if (layout == OR_LAYOUT_ZIGZAG) {
+        const long long half = block_len / 2;
+        if (r < half)
+            return (long long)host * half + r;
+        return (long long)(2 * n_hosts - 1 - host) * half + (r - half);
+    }
     return (long long)host * block_len + r;
 }
 

@@ -23,6 +23,7 @@ import numpy as np
 
 LAYOUT_CONTIGUOUS = 0
 LAYOUT_STRIPED = 1
+LAYOUT_ZIGZAG = 2
 MASK_NONE = 0
 MASK_CAUSAL = 1
 DT_BF16 = 0
@@ -43,7 +44,7 @@ class Workload:
     block_len: int
     dtype: int               # DT_BF16 or DT_F32
     mask: int                # MASK_NONE or MASK_CAUSAL
-    layout: int              # LAYOUT_CONTIGUOUS or LAYOUT_STRIPED
+    layout: int              # LAYOUT_CONTIGUOUS, LAYOUT_STRIPED or LAYOUT_ZIGZAG
     host_begin: int
     host_end: int
     q_scale: float = 1.0     # multiplies Q before rounding (large-logit variant)
@@ -76,6 +77,8 @@ def workloads() -> dict:
                                        MASK_CAUSAL, LAYOUT_CONTIGUOUS, 7, 8)
     w["causal_256k_striped"] = w["causal_256k_contig"].replace(
         name="causal_256k_striped_H32_N8_c32768_host7", layout=LAYOUT_STRIPED)
+    w["causal_256k_zigzag"] = w["causal_256k_contig"].replace(
+        name="causal_256k_zigzag_H32_N8_c32768_host7", layout=LAYOUT_ZIGZAG)
     w["striped_786k_gqa"] = Workload("striped_786k_gqa_Hq32_Hkv8_N16_c49152_host15",
                                      4, 1, 32, 8, 128, 16, 49152, DT_BF16,
                                      MASK_CAUSAL, LAYOUT_STRIPED, 15, 16)

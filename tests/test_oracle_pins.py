@@ -17,7 +17,7 @@ import pytest
 from oracle import cref, npref
 import ra_synth as rs
 
-C, S = rs.LAYOUT_CONTIGUOUS, rs.LAYOUT_STRIPED
+C, S, Z = rs.LAYOUT_CONTIGUOUS, rs.LAYOUT_STRIPED, rs.LAYOUT_ZIGZAG
 
 
 def _rand(seed, shape, scale=1.0):
@@ -93,10 +93,39 @@ def test_striped_masks_are_triangles():
             assert np.array_equal(m, tri_incl if j <= i else tri_strict)
 
 
+@pytest.mark.parametrize("N,c", [(1, 2), (2, 4), (3, 6), (4, 128), (8, 10)])
+def test_zigzag_token_map_is_a_bijection(N, c):
+    """Zigzag places every token of the sequence on exactly one (host, row)."""
+    tc = sorted(cref.token_index(Z, N, c, h, r) for h in range(N) for r in range(c))
+    tn = np.sort(np.concatenate([npref.token_index(Z, N, c, h, np.arange(c)) for h in range(N)]))
+    assert tc == list(range(N * c))
+    assert np.array_equal(tn, np.arange(N * c))
+
+
+@pytest.mark.parametrize("N,c", [(2, 4), (3, 6), (4, 8), (8, 16)])
+def test_zigzag_balances_causal_work(N, c):
+    """The pages name Zigzag beside Striped as the causal layout that avoids
+    load imbalance (P1, 工程实践指南, 因果掩码).  Closed form: every host sees
+    exactly S(S+1)/(2N) visible (query, key) pairs, S = N c (half h = c/2:
+    h^2 (2N-1) + h (h+1) per host), while contiguous hosts differ."""
+    S_ = N * c
+    h = c // 2
+    want = S_ * (S_ + 1) // (2 * N)
+    assert want == h * h * (2 * N - 1) + h * (h + 1)
+    contig = []
+    for i in range(N):
+        got = sum(int(cref.block_mask(Z, 1, N, c, i, j).sum()) for j in range(N))
+        assert got == want, (i, got, want)
+        contig.append(sum(int(cref.block_mask(C, 1, N, c, i, j).sum()) for j in range(N)))
+    assert len(set(contig)) == N                       # contiguous: every host differs
+
+
 def test_mask_c_vs_numpy():
-    for layout in (C, S):
+    for layout in (C, S, Z):
         for causal in (0, 1):
             for N, c in ((3, 5), (4, 4), (5, 2)):
+                if layout == Z and c % 2:
+                    continue
                 for i in range(N):
                     for j in range(N):
                         mc = cref.block_mask(layout, causal, N, c, i, j)
@@ -110,7 +139,7 @@ def test_mask_c_vs_numpy():
 # forward definition
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("layout,causal", [(C, 0), (C, 1), (S, 1)])
+@pytest.mark.parametrize("layout,causal", [(C, 0), (C, 1), (S, 1), (Z, 1)])
 @pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2)])
 def test_forward_vs_brute_force(layout, causal, hq, hkv):
     N, B, c, d = 3, 2, 4, 5
@@ -175,7 +204,7 @@ def test_causal_library_sdpa_full_sequence():
             assert np.allclose(O[h], ref[:, t].numpy(), atol=1e-12, rtol=0)
 
 
-@pytest.mark.parametrize("layout,causal", [(C, 0), (C, 1), (S, 1)])
+@pytest.mark.parametrize("layout,causal", [(C, 0), (C, 1), (S, 1), (Z, 1)])
 def test_numpy_dense_matches_c(layout, causal):
     N, B, H, c, d = 4, 1, 2, 8, 16
     q = _rand(41, (N, B, H, c, d)); k = _rand(42, (N, B, H, c, d)); v = _rand(43, (N, B, H, c, d))
@@ -198,7 +227,7 @@ def test_numpy_dense_matches_c(layout, causal):
 # blocked ring procedure: equals the definition, in any block order
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("layout,causal", [(C, 0), (C, 1), (S, 1)])
+@pytest.mark.parametrize("layout,causal", [(C, 0), (C, 1), (S, 1), (Z, 1)])
 def test_blocked_ring_all_orders(layout, causal):
     N, c, d = 4, 6, 8
     q = _rand(51, (N, 1, 1, c, d), 3.0)
@@ -286,11 +315,11 @@ def test_merge_with_empty_parts():
 # closed forms (these also run at full scale against the GPU)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("layout", [C, S])
+@pytest.mark.parametrize("layout", [C, S, Z])
 def test_closed_form_q_zero(layout):
     """Q = 0: every visible score is 0, so l = number of visible keys,
     LSE = ln(count), O = mean of V over visible keys (count = t_q + 1 causal)."""
-    N, c, d = 4, 7, 5
+    N, c, d = 4, (8 if layout == Z else 7), 5             # zigzag halves need even c
     q = np.zeros((N, 1, 1, c, d), np.float32)
     k = _rand(81, (N, 1, 1, c, d)); v = _rand(82, (N, 1, 1, c, d))
     O, lse, mx, l = cref.attn_rows(q, k, v, n_hosts=N, layout=layout, causal=1,
