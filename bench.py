@@ -48,6 +48,8 @@ def counted_pairs(w, host):
         return N * c * c
     if w.layout == rs.LAYOUT_CONTIGUOUS:
         return host * c * c + c * (c + 1) // 2
+    if w.layout == rs.LAYOUT_ZIGZAG:       # chunks h and 2N-1-h of c/2 tokens: the same on every host
+        return c * (N * c + 1) // 2
     return (host + 1) * c * (c + 1) // 2 + (N - 1 - host) * c * (c - 1) // 2
 
 
@@ -273,23 +275,22 @@ def reference_gemm(torch, n=8192, reps=20):
 
 
 def causal_rates(torch, ra, steps=3):
-    """Forward TFLOP/s of the causal 256K host-7 workload in both layouts and
-    of the 786K striped GQA host-15 workload (seeded device-side inputs)."""
+    """Forward TFLOP/s of the causal 256K host-7 workload in the contiguous,
+    striped and zigzag layouts and of the 786K striped GQA host-15 workload
+    (seeded device-side inputs)."""
     out = {}
     wl = rs.workloads()
-    for key in ("causal_256k_contig", "causal_256k_striped", "striped_786k_gqa"):
+    for key in ("causal_256k_contig", "causal_256k_striped", "causal_256k_zigzag", "striped_786k_gqa"):
         w = wl[key]
         ring = Ring(w, torch, ra, seed=w.cfg)
         ring.fwd()
         torch.cuda.synchronize()
         wall, gpu_ms, f_ms, _ = time_ring(ring, steps, 0, False)
         fl = counted_flops(w, 4)
-        active = [t for t in f_ms if t > 0.01]
         out[key] = {"ms": gpu_ms / steps, "tflops": fl / (gpu_ms / steps / 1e3) / 1e12,
                     "kernel_ms_per_step": sum(f_ms) / steps}
         del ring
         torch.cuda.empty_cache()
-    nc = None
     return out
 
 

@@ -71,8 +71,16 @@ typedef enum { RA_BF16 = 0, RA_F32 = 1 } ra_dtype;
 typedef enum { RA_MASK_NONE = 0, RA_MASK_CAUSAL = 1 } ra_mask_mode;
 
 /* Token layout ([P1] 因果掩码的负载均衡挑战): contiguous = host h holds
- * tokens h*c .. h*c + c - 1; striped = host h holds tokens h, h+N, h+2N, ... */
-typedef enum { RA_LAYOUT_CONTIGUOUS = 0, RA_LAYOUT_STRIPED = 1 } ra_layout;
+ * tokens h*c .. h*c + c - 1; striped = host h holds tokens h, h+N, h+2N, ...
+ * zigzag ([P1] 工程实践指南, item 因果掩码, names it beside Striped as the
+ * causal load-balancing variant without defining it; the reading used here):
+ * the sequence is cut into 2N chunks of c/2 tokens, host h holds chunk h in
+ * rows 0..c/2-1 and chunk 2N-1-h in rows c/2..c-1, so every host sees the
+ * same number of causal (query, key) pairs.  Zigzag needs an even block_len
+ * (the scheduler and token index) and, in the ring forward, bf16 blocks with
+ * block_len % 256 == 0; the backward and the block calls take contiguous or
+ * striped only. */
+typedef enum { RA_LAYOUT_CONTIGUOUS = 0, RA_LAYOUT_STRIPED = 1, RA_LAYOUT_ZIGZAG = 2 } ra_layout;
 
 /* What a (query block, key block) pair needs under the mask.
  * SKIP: no visible pair ([P3] 工程实现: blocks j > i are skipped);
@@ -83,7 +91,9 @@ typedef enum {
     RA_BLK_FULL = 1,
     RA_BLK_TRI_INCL = 2,
     RA_BLK_TRI_STRICT = 3,
-    RA_BLK_BAND = 4 /* any other diagonal band (general offsets) */
+    RA_BLK_BAND = 4, /* any other diagonal band (general offsets) */
+    RA_BLK_QUADRANTS = 5 /* zigzag causal: the four (c/2 x c/2) quadrants of the
+                            block pair each have their own class */
 } ra_block_class;
 
 typedef struct {
@@ -153,6 +163,11 @@ int64_t ra_token_index(int32_t layout, int32_t n_hosts, int64_t block_len, int32
  * r iff kv_offset + r'*stride <= q_offset + r*stride (causal) -- for
  * contiguous: FULL for src < host, TRI_INCL for src == host, SKIP for
  * src > host; for striped: TRI_INCL for src <= host, TRI_STRICT otherwise.
+ * Zigzag (block_len even): q_offset, kv_offset are the first tokens of the
+ * two blocks' first chunks (host*c/2, src*c/2), stride 1, and the class is
+ * QUADRANTS under the causal mask (FULL otherwise): the block pair splits
+ * into four c/2 x c/2 quadrants between chunk a of the query block and chunk
+ * b of the key block, each contiguous with its own offsets.
  * out: host array of n_hosts entries, written in step order. */
 ra_status ra_schedule(int32_t n_hosts, int32_t host, int32_t block_len, int32_t layout,
                       int32_t mask, ra_step *out);

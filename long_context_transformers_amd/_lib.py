@@ -15,8 +15,8 @@ LIB_PATH = os.path.join(_HERE, "libringattn.so")
 RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_HIP, RA_ERR_WORKSPACE = range(5)
 RA_BF16, RA_F32 = 0, 1
 RA_MASK_NONE, RA_MASK_CAUSAL = 0, 1
-RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED = 0, 1
-RA_BLK_SKIP, RA_BLK_FULL, RA_BLK_TRI_INCL, RA_BLK_TRI_STRICT, RA_BLK_BAND = range(5)
+RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED, RA_LAYOUT_ZIGZAG = 0, 1, 2
+RA_BLK_SKIP, RA_BLK_FULL, RA_BLK_TRI_INCL, RA_BLK_TRI_STRICT, RA_BLK_BAND, RA_BLK_QUADRANTS = range(6)
 RA_FLAG_ELIDE_SKIPPED_COPIES = 1
 RA_FLAG_SERIALIZE = 2
 

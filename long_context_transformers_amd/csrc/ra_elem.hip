@@ -179,7 +179,9 @@ hipError_t launch_bwd_pre(const void* o, const void* dO, float* D, int64_t rows,
 }
 
 // Token-layout permutation: host-major row (h, b, head, r) <-> full row
-// (b, head, t) with t = h*c + r (contiguous) or r*N + h (striped).
+// (b, head, t) with t = h*c + r (contiguous), r*N + h (striped) or, zigzag
+// (c even, half = c/2), h*half + r for r < half and (2N-1-h)*half + r - half
+// otherwise.
 __global__ void permute_kernel(const uint4* src, uint4* dst, int batch, int heads, int n_hosts, int c,
                                int chunks, int layout, int to_host_major) {
   const int64_t n = (int64_t)n_hosts * batch * heads * c * chunks;
@@ -192,7 +194,10 @@ __global__ void permute_kernel(const uint4* src, uint4* dst, int batch, int head
     const int hd = (int)(x % heads); x /= heads;
     const int b = (int)(x % batch);
     const int h = (int)(x / batch);
-    const int64_t t = layout == 1 ? r * n_hosts + h : (int64_t)h * c + r;
+    const int64_t half = c / 2;
+    const int64_t t = layout == 1   ? r * n_hosts + h
+                      : layout == 2 ? (r < half ? (int64_t)h * half + r : (int64_t)(2 * n_hosts - 1 - h) * half + (r - half))
+                                    : (int64_t)h * c + r;
     const int64_t full = (((int64_t)b * heads + hd) * S + t) * chunks + ch;
     if (to_host_major) dst[i] = src[full];
     else dst[full] = src[i];

@@ -100,16 +100,31 @@ void fwd_bf16_kernel(FwdArgs a) {
   logical /= n_hg;
   const int b = logical % a.batch;
   const int host = logical / a.batch;
-  const int delta = a.delta[host];
 
   const int q0 = rt * ROWS;
   const int row_last = min(q0 + ROWS, c) - 1;
-  const int kend = min(c, row_last + delta + 1);   // keys [0, kend) can be visible
-  if (kend <= 0) return;                           // nothing visible: state unchanged
-  const int ntiles = (kend + kBN - 1) / kBN;
-  // leading tiles where every (row, key) pair of the workgroup is visible and in range
-  int n_unmasked = min((delta + q0 - (kBN - 1)) >= 0 ? (delta + q0 - (kBN - 1)) / kBN + 1 : 0, c / kBN);
-  n_unmasked = min(n_unmasked, ntiles);
+  // Key segments with one visibility offset each: the whole block, or, for a
+  // zigzag block (zz_half = c/2, a multiple of ROWS), the two key halves seen
+  // from this row tile's query half.  Segment sg covers key tiles
+  // [sb, se): a fully visible, complete prefix [sb, su) runs without masks,
+  // [su, se) (up to the last key any row of the tile can see) with masks.
+  const int zh = a.zz_half;
+  int sb[2], su[2], se[2], sd[2];
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg) {
+    const int lo = zh ? sg * zh : 0, hi = zh ? lo + zh : c;
+    const int d = zh ? a.delta4[host][2 * (q0 >= zh ? 1 : 0) + sg] : a.delta[host];
+    const int kend = min(hi, row_last + d + 1);     // keys [lo, kend) can be visible
+    const int tb = lo / kBN, te = kend > lo ? (kend + kBN - 1) / kBN : tb;
+    int tu = (d + q0 - (kBN - 1)) >= 0 ? (d + q0 - (kBN - 1)) / kBN + 1 : 0;
+    tu = max(tb, min(min(tu, c / kBN), te));
+    const bool used = (sg == 0 || zh) && te > tb;
+    sb[sg] = tb;
+    su[sg] = used ? tu : tb;
+    se[sg] = used ? te : tb;
+    sd[sg] = d;
+  }
+  if (se[0] <= sb[0] && se[1] <= sb[1]) return;    // nothing visible: state unchanged
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -203,13 +218,16 @@ void fwd_bf16_kernel(FwdArgs a) {
   //  O^T += V^T P^T over key steps kq (32 keys): slot v = (kq, nt) reads the
   //  transposed V operand; P^T's item j of lane (g, i) is key 32kq + 16(j/4)
   //  + 4g + j%4, the order in which the transposing read delivers V.
-  auto step = [&](int t, auto masked) {
-    if (t + 1 < ntiles) {
-      dma_k(t + 1, (t + 1) & 1);
-      dma_v(t + 1, (t + 1) & 1);
+  // tile t (keys [64t, 64t+64)) in LDS buffer `buf`; tile tn (-1: none) is
+  // prefetched into the other buffer; delta is the current segment's offset
+  int delta = sd[0];
+  auto step = [&](int t, int tn, int buf, auto masked) {
+    if (tn >= 0) {
+      dma_k(tn, buf ^ 1);
+      dma_v(tn, buf ^ 1);
     }
-    const unsigned char* ks = smem + (t & 1) * TILE;
-    const unsigned char* vs = smem + (2 + (t & 1)) * TILE;
+    const unsigned char* ks = smem + buf * TILE;
+    const unsigned char* vs = smem + (2 + buf) * TILE;
     const int kb0 = t * kBN;
     constexpr int NU = 4 * NKK, NC = 2 * NT, kPre = 2;
     f32x4 s[4][2];
@@ -294,12 +312,22 @@ void fwd_bf16_kernel(FwdArgs a) {
     tile::dma_wait();
     __syncthreads();
   };
-  dma_k(0, 0);
-  dma_v(0, 0);
+  const int t_first = se[0] > sb[0] ? sb[0] : sb[1];
+  dma_k(t_first, 0);
+  dma_v(t_first, 0);
   tile::dma_wait();
   __syncthreads();
-  for (int t = 0; t < n_unmasked; ++t) step(t, std::false_type{});
-  for (int t = n_unmasked; t < ntiles; ++t) step(t, std::true_type{});
+  int buf = 0;
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg) {
+    if (se[sg] > sb[sg]) {
+      delta = sd[sg];
+      const int te = se[sg];
+      const int tnext = (sg == 0 && se[1] > sb[1]) ? sb[1] : -1;
+      for (int t = sb[sg]; t < su[sg]; ++t, buf ^= 1) step(t, t + 1 < te ? t + 1 : tnext, buf, std::false_type{});
+      for (int t = su[sg]; t < te; ++t, buf ^= 1) step(t, t + 1 < te ? t + 1 : tnext, buf, std::true_type{});
+    }
+  }
 
   // ---- write the state back, referenced to the true running max ----
 #pragma unroll

@@ -151,8 +151,10 @@ ra_status check_cfg(const ra_ring_cfg* c) {
   if (c->host_begin < 0 || c->host_end > c->n_hosts || c->host_begin >= c->host_end)
     return fail(RA_ERR_INVALID_ARG, "host range [%d, %d) invalid for %d hosts", c->host_begin, c->host_end,
                 c->n_hosts);
-  if (c->layout != RA_LAYOUT_CONTIGUOUS && c->layout != RA_LAYOUT_STRIPED)
+  if (c->layout != RA_LAYOUT_CONTIGUOUS && c->layout != RA_LAYOUT_STRIPED && c->layout != RA_LAYOUT_ZIGZAG)
     return fail(RA_ERR_INVALID_ARG, "unknown layout %d", c->layout);
+  if (c->layout == RA_LAYOUT_ZIGZAG && (c->dims.block_len % 2) != 0)
+    return fail(RA_ERR_INVALID_ARG, "zigzag needs an even block_len (got %d)", c->dims.block_len);
   if (c->mask != RA_MASK_NONE && c->mask != RA_MASK_CAUSAL) return fail(RA_ERR_INVALID_ARG, "unknown mask %d", c->mask);
   if (c->flags & ~(RA_FLAG_ELIDE_SKIPPED_COPIES | RA_FLAG_SERIALIZE))
     return fail(RA_ERR_INVALID_ARG, "unknown flag bits 0x%x", c->flags);
@@ -167,6 +169,14 @@ void schedule_one(int32_t N, int32_t host, int32_t c, int32_t layout, int32_t ma
   o->step = s;
   o->src = j;
   o->pad_ = 0;
+  if (layout == RA_LAYOUT_ZIGZAG) {
+    // first tokens of the two blocks' first chunks; the quadrants carry the rest
+    o->q_offset = (int64_t)host * (c / 2);
+    o->kv_offset = (int64_t)j * (c / 2);
+    o->stride = 1;
+    o->cls = mask == RA_MASK_NONE ? RA_BLK_FULL : RA_BLK_QUADRANTS;
+    return;
+  }
   if (layout == RA_LAYOUT_STRIPED) {
     o->q_offset = host;
     o->kv_offset = j;
@@ -178,6 +188,21 @@ void schedule_one(int32_t N, int32_t host, int32_t c, int32_t layout, int32_t ma
   }
   o->cls = mask == RA_MASK_NONE ? RA_BLK_FULL
                                 : class_of_delta(compute_delta(mask, o->q_offset, o->kv_offset, o->stride, c), c);
+}
+
+// Zigzag block pair (query host `host`, key block `src`), half h = c/2:
+// query rows of quadrant a hold chunk (a ? 2N-1-host : host), key rows of
+// quadrant b chunk (b ? 2N-1-src : src), chunk q covering tokens
+// [q h, q h + h).  Within a quadrant key row r' is visible to query row r
+// iff r' - r <= delta4[2a + b] in block-local rows.
+void zz_delta4(int32_t mask, int32_t N, int32_t host, int32_t src, int32_t c, int32_t* d4) {
+  const int32_t h = c / 2;
+  for (int a = 0; a < 2; ++a)
+    for (int b = 0; b < 2; ++b) {
+      const int64_t qo = (int64_t)(a ? 2 * N - 1 - host : host) * h;
+      const int64_t ko = (int64_t)(b ? 2 * N - 1 - src : src) * h;
+      d4[2 * a + b] = compute_delta(mask, qo, ko, 1, h) + (b - a) * h;
+    }
 }
 
 // Events of one ring call; destroyed on every exit path.
@@ -264,6 +289,10 @@ int64_t ra_token_index(int32_t layout, int32_t n_hosts, int64_t block_len, int32
   if (n_hosts < 1 || block_len < 1 || host < 0 || host >= n_hosts || r < 0 || r >= block_len) return -1;
   if (layout == RA_LAYOUT_STRIPED) return r * n_hosts + host;
   if (layout == RA_LAYOUT_CONTIGUOUS) return (int64_t)host * block_len + r;
+  if (layout == RA_LAYOUT_ZIGZAG && block_len % 2 == 0) {
+    const int64_t half = block_len / 2;
+    return r < half ? (int64_t)host * half + r : (int64_t)(2 * n_hosts - 1 - host) * half + (r - half);
+  }
   return -1;
 }
 
@@ -277,8 +306,10 @@ ra_status ra_schedule(int32_t n_hosts, int32_t host, int32_t block_len, int32_t 
                       ra_step* out) {
   if (n_hosts < 1 || host < 0 || host >= n_hosts || block_len < 1)
     return fail(RA_ERR_INVALID_ARG, "ra_schedule: bad n_hosts/host/block_len (%d, %d, %d)", n_hosts, host, block_len);
-  if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED)
+  if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED && layout != RA_LAYOUT_ZIGZAG)
     return fail(RA_ERR_INVALID_ARG, "ra_schedule: unknown layout %d", layout);
+  if (layout == RA_LAYOUT_ZIGZAG && block_len % 2 != 0)
+    return fail(RA_ERR_INVALID_ARG, "ra_schedule: zigzag needs an even block_len (got %d)", block_len);
   if (mask != RA_MASK_NONE && mask != RA_MASK_CAUSAL) return fail(RA_ERR_INVALID_ARG, "ra_schedule: unknown mask %d", mask);
   if (!out) return fail(RA_ERR_INVALID_ARG, "ra_schedule: out is NULL");
   for (int32_t s = 0; s < n_hosts; ++s) schedule_one(n_hosts, host, block_len, layout, mask, s, &out[s]);
@@ -399,8 +430,10 @@ ra_status ra_layout_permute(const ra_dims* dims, int32_t heads, int32_t n_hosts,
   RA_CHECK(check_dims(dims));
   if (heads < 1) return fail(RA_ERR_INVALID_ARG, "heads must be >= 1");
   if (n_hosts < 1) return fail(RA_ERR_INVALID_ARG, "n_hosts must be >= 1");
-  if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED)
+  if (layout != RA_LAYOUT_CONTIGUOUS && layout != RA_LAYOUT_STRIPED && layout != RA_LAYOUT_ZIGZAG)
     return fail(RA_ERR_INVALID_ARG, "unknown layout %d", layout);
+  if (layout == RA_LAYOUT_ZIGZAG && dims->block_len % 2 != 0)
+    return fail(RA_ERR_INVALID_ARG, "zigzag needs an even block_len (got %d)", dims->block_len);
   RA_CHECK(check_ptr(src, "src"));
   RA_CHECK(check_ptr(dst, "dst"));
   if (src == dst) return fail(RA_ERR_INVALID_ARG, "src and dst must not alias");
@@ -443,6 +476,12 @@ ra_status ra_ring_fwd(const ra_ring_cfg* cfg, const void* Q, const void* K, cons
   const FwdWs w = fwd_ws(cfg);
   if (workspace_bytes < w.total)
     return fail(RA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, w.total);
+  // zigzag under the causal mask: quadrant-wise masking in the bf16 kernel,
+  // whose query row tiles (up to 128 rows) must not straddle the two halves
+  const bool zz = cfg->layout == RA_LAYOUT_ZIGZAG && cfg->mask == RA_MASK_CAUSAL;
+  if (zz && (cfg->dims.dtype != RA_BF16 || cfg->dims.block_len % 256 != 0))
+    return fail(RA_ERR_UNSUPPORTED, "causal zigzag ring forward needs bf16 and block_len %% 256 == 0 (got %d)",
+                cfg->dims.block_len);
 
   const ra_dims* d = &cfg->dims;
   const int N = cfg->n_hosts, hb = cfg->host_begin, na = cfg->host_end - cfg->host_begin;
@@ -496,9 +535,15 @@ ra_status ra_ring_fwd(const ra_ring_cfg* cfg, const void* Q, const void* K, cons
       args.batch = d->batch; args.hq = d->heads_q; args.hkv = d->heads_kv; args.c = d->block_len; args.n_hosts = cnt;
       args.scale_log2 = eff_scale(d) * kLog2e;
       bool any = false;
+      args.zz_half = zz ? d->block_len / 2 : 0;
       for (int i = 0; i < cnt; ++i) {
         const ra_step& stp = sched[(size_t)(a0 + i) * N + s];
-        args.delta[i] = compute_delta(cfg->mask, stp.q_offset, stp.kv_offset, stp.stride, d->block_len);
+        if (zz) {
+          args.delta[i] = d->block_len;
+          zz_delta4(cfg->mask, N, hb + a0 + i, stp.src, d->block_len, args.delta4[i]);
+        } else {
+          args.delta[i] = compute_delta(cfg->mask, stp.q_offset, stp.kv_offset, stp.stride, d->block_len);
+        }
         if (stp.cls == RA_BLK_SKIP) st.skipped_blocks++;
         else any = true;
       }
@@ -526,6 +571,8 @@ ra_status ra_ring_bwd(const ra_ring_cfg* cfg, const void* Q, const void* K, cons
   RA_CHECK(check_cfg(cfg));
   if (cfg->host_begin != 0 || cfg->host_end != cfg->n_hosts)
     return fail(RA_ERR_UNSUPPORTED, "ring backward runs every host (host_begin = 0, host_end = n_hosts)");
+  if (cfg->layout == RA_LAYOUT_ZIGZAG)
+    return fail(RA_ERR_UNSUPPORTED, "ring backward takes contiguous or striped layouts");
   if (cfg->flags & RA_FLAG_ELIDE_SKIPPED_COPIES)
     return fail(RA_ERR_INVALID_ARG, "copy elision does not apply to the full ring");
   RA_CHECK(check_ptr(Q, "Q"));

@@ -33,6 +33,11 @@ struct FwdArgs {
   int32_t batch, hq, hkv, c, n_hosts;
   float scale_log2;        // score scale * log2(e)
   int32_t delta[kMaxHostsPerLaunch];
+  // Zigzag blocks: zz_half = c/2 (0 for other layouts); key row r' (block
+  // local) is visible to query row r in quadrant (a = r / zz_half,
+  // b = r' / zz_half) iff r' - r <= delta4[host][2a + b].
+  int32_t zz_half;
+  int32_t delta4[kMaxHostsPerLaunch][4];
 };
 
 // Backward launch arguments (same host striding convention).

@@ -19,6 +19,7 @@ import pytest
 
 import long_context_transformers_amd as ra
 from long_context_transformers_amd import _lib as L
+import ra_synth as rs
 from oracle import cref
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -66,6 +67,26 @@ def test_schedule_bit_exact_vs_oracle_masks(layout, mask):
                     assert np.array_equal(_CLASS_PATTERN[s["cls"]](c), want), (N, c, i, s)
 
 
+@pytest.mark.parametrize("mask", [ra.RA_MASK_NONE, ra.RA_MASK_CAUSAL])
+def test_schedule_zigzag(mask):
+    """Zigzag steps: ring order, first-chunk offsets (stride 1), class
+    QUADRANTS under the causal mask; quadrant (0, 0) -- chunk i against
+    chunk src -- is exactly the oracle's mask on those rows and keys."""
+    Z = ra.RA_LAYOUT_ZIGZAG
+    for N in (1, 2, 3, 4, 8):
+        for c in (2, 4, 8, 64):
+            h = c // 2
+            for i in range(N):
+                steps = ra.schedule(N, i, c, Z, mask)
+                assert [s["src"] for s in steps] == [(i - s) % N for s in range(N)]
+                for s in steps:
+                    j = s["src"]
+                    assert (s["q_offset"], s["kv_offset"], s["stride"]) == (i * h, j * h, 1)
+                    assert s["cls"] == (ra.RA_BLK_FULL if mask == ra.RA_MASK_NONE else ra.RA_BLK_QUADRANTS)
+                    want = cref.block_mask(Z, mask, N, c, i, j).astype(bool)
+                    assert np.array_equal(_implied_mask(s, h, mask), want[:h, :h]), (N, c, i, s)
+
+
 def test_schedule_ring_holdings(golden_dir):
     g = json.load(open(os.path.join(golden_dir, "ring_holdings_N4.json")))
     for step, held in g["held"].items():
@@ -96,6 +117,11 @@ def test_token_index_golden(golden_dir):
             assert ra.token_index(C, 5, 7, h, r) == cref.token_index(C, 5, 7, h, r)
             assert ra.token_index(S, 5, 7, h, r) == cref.token_index(S, 5, 7, h, r)
     assert ra.token_index(S, 4, 10, 4, 0) == -1 and ra.token_index(C, 4, 10, 0, 10) == -1
+    Z = ra.RA_LAYOUT_ZIGZAG
+    for N, c in ((1, 2), (3, 6), (4, 8), (8, 256)):
+        got = [ra.token_index(Z, N, c, h, r) for h in range(N) for r in range(c)]
+        assert got == [cref.token_index(Z, N, c, h, r) for h in range(N) for r in range(c)]
+    assert ra.token_index(Z, 4, 7, 0, 0) == -1                       # odd block_len
 
 
 def test_block_class_general_offsets():
@@ -190,13 +216,21 @@ def test_ring_argument_checks():
     assert _ring_fwd(cfg, need, ws=0x100010) == L.RA_ERR_INVALID_ARG   # not 256-aligned
     assert _ring_fwd(_cfg(host_begin=3, host_end=3), need) == L.RA_ERR_INVALID_ARG
     assert _ring_fwd(_cfg(host_end=9), need) == L.RA_ERR_INVALID_ARG
-    assert _ring_fwd(_cfg(layout=2), need) == L.RA_ERR_INVALID_ARG
+    assert _ring_fwd(_cfg(layout=7), need) == L.RA_ERR_INVALID_ARG
     assert _ring_fwd(_cfg(flags=0x80), need) == L.RA_ERR_INVALID_ARG
     assert _ring_fwd(_cfg(n_hosts=0), need) == L.RA_ERR_INVALID_ARG
+    # zigzag: even block_len; the causal ring forward needs bf16 and c % 256 == 0
+    Z = ra.RA_LAYOUT_ZIGZAG
+    big = 1 << 40
+    assert _ring_fwd(_cfg(layout=Z, dims=_dims(block_len=63)), big) == L.RA_ERR_INVALID_ARG
+    assert _ring_fwd(_cfg(layout=Z, mask=1, dims=_dims(block_len=64)), big) == L.RA_ERR_UNSUPPORTED
+    assert _ring_fwd(_cfg(layout=Z, mask=1, dims=_dims(block_len=256, dtype=1)), big) == L.RA_ERR_UNSUPPORTED
     st = L.RaRingStats()
-    # backward: partial host ranges are not supported
+    # backward: partial host ranges and zigzag are not supported
     assert ra.raw_call("ra_ring_bwd", ctypes.byref(_cfg(host_begin=7)), *([FAKE] * 10), 1 << 40,
                        None, None, ctypes.byref(st)) == L.RA_ERR_UNSUPPORTED
+    assert ra.raw_call("ra_ring_bwd", ctypes.byref(_cfg(layout=Z, dims=_dims(block_len=256))), *([FAKE] * 10),
+                       1 << 40, None, None, ctypes.byref(st)) == L.RA_ERR_UNSUPPORTED
 
 
 def test_workspace_size_formula():
@@ -233,3 +267,16 @@ def test_overlap_threshold_table(golden_dir):
     assert ra.overlap.block_flops(128, 1024) == 4 * 128 * 1024 ** 2
     assert ra.overlap.kv_transfer_bytes(128, 1024) == 4 * 1024 * 128
     assert ra.overlap.ring_time(8, 2.0, 3.0) == 24.0
+
+
+def test_bench_pair_count_matches_oracle_masks():
+    """bench.py counts visible (query, key) pairs in closed form per layout;
+    the oracle's block masks summed over the ring must give the same."""
+    import bench
+    for layout in (rs.LAYOUT_CONTIGUOUS, rs.LAYOUT_STRIPED, rs.LAYOUT_ZIGZAG):
+        for mask in (rs.MASK_NONE, rs.MASK_CAUSAL):
+            for N, c in ((1, 8), (3, 6), (4, 10)):
+                w = rs.Workload("count", 0, 1, 1, 1, 64, N, c, rs.DT_BF16, mask, layout, 0, N)
+                for h in range(N):
+                    want = sum(int(cref.block_mask(layout, mask, N, c, h, j).sum()) for j in range(N))
+                    assert bench.counted_pairs(w, h) == want, (layout, mask, N, c, h)
