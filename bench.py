@@ -294,6 +294,62 @@ def causal_rates(torch, ra, steps=3):
     return out
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "ring_bwd_step_noncausal_32k_hbm_traffic.md")
+BWD_SOURCES = [os.path.join(ROOT, "long_context_transformers_amd", "csrc", n)
+               for n in ("ra_bwd.hip", "ra_tile.h", "ra_internal.h")]
+
+
+def bwd_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for p in BWD_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per backward ring step (dK/dV + dQ kernels) from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when the kernel sources
+    have changed since the counters were taken (or no summary exists)."""
+    import re
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    vals = dict(re.findall(r"^- (\w+): `([^`]+)`", text, re.M))
+    if vals.get("sources_sha256") != bwd_sources_sha256():
+        return None
+    return float(vals["fetch_bytes_per_step"]) + float(vals["write_bytes_per_step"])
+
+
+def bwd_algorithmic_bytes(w):
+    """Bytes one backward ring step moves for all hosts, averaged over a ring
+    pass: the dK/dV kernel reads Q, dO, K, V (bf16), lse, D (fp32) and the
+    received dK/dV partial sums (fp32; none at the first step) and writes the
+    new sums; the dQ kernel reads Q, dO, K, V, lse, D and the fp32 dQ sum (none
+    at the first step) and writes it.  Non-causal: every block is whole."""
+    N, c, d = w.n_hosts, w.block_len, w.head_dim
+    hq, hkv = w.batch * w.heads_q, w.batch * w.heads_kv
+    qo = 2 * hq * c * d * 2 + 2 * hq * c * 4         # Q, dO, lse, D
+    kv = 2 * hkv * c * d * 2                         # K, V
+    dkdv = 2 * hkv * c * d * 4                       # dK and dV sums, one direction
+    dq = hq * c * d * 4                              # dQ sum, one direction
+    per_host = 2 * (qo + kv) + (dkdv + dq) * (1 + (N - 1) / N)
+    return N * per_host
+
+
+def copy_calibration(torch, mib, reps=5):
+    """Plain device copy of a known size, for scaling the HBM counters."""
+    n = mib << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -303,6 +359,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (HBM counter scaling) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -314,6 +372,9 @@ def main():
     import long_context_transformers_amd as ra
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     ra.version()
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration)
+        return
 
     w = rs.workloads()["noncausal_32k"]
     log(f"[bench] workload {w.name}: drawing inputs")
@@ -341,15 +402,19 @@ def main():
     b_launch = statistics.mean(b_ms) if bwd else 0.0
     if b_launch * 1 > f_launch:
         dom = {"kernel": "block backward (dK/dV + dQ kernels of one ring step, all hosts)",
-               "flops_per_launch": bwd_flops / N, "avg_launch_ms": b_launch}
+               "flops_per_launch": bwd_flops / N, "avg_launch_ms": b_launch,
+               "traffic": measured_traffic(), "algorithmic_bytes_per_launch": bwd_algorithmic_bytes(w)}
     else:
         dom = {"kernel": "fwd_bf16_kernel (one ring step, all 8 hosts)",
-               "flops_per_launch": fwd_flops / N, "avg_launch_ms": f_launch}
+               "flops_per_launch": fwd_flops / N, "avg_launch_ms": f_launch, "traffic": None,
+               "algorithmic_bytes_per_launch": None}
     achieved = dom["flops_per_launch"] / (dom["avg_launch_ms"] / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": dom["traffic"],
                 "kernel": dom["kernel"], "avg_launch_ms": dom["avg_launch_ms"],
-                "algorithmic_flops_per_launch": dom["flops_per_launch"]}
+                "algorithmic_flops_per_launch": dom["flops_per_launch"],
+                "algorithmic_bytes_per_launch": dom["algorithmic_bytes_per_launch"],
+                "traffic_source": os.path.relpath(TRAFFIC_PROFILE, ROOT)}
 
     extra = {"fwd_tflops": fwd_flops / (sum(f_ms) / args.steps / 1e3) / 1e12,
              "fwd_kernel_avg_launch_ms": f_launch,
