@@ -350,6 +350,26 @@ def copy_calibration(torch, mib, reps=5):
     print(json.dumps({"copy_calibration_bytes": n, "reps": reps}), flush=True)
 
 
+def bwd_rates(torch, ra, steps=2):
+    """Ring forward + backward of the causal 64K workload (32 heads, d = 128,
+    8 hosts x 8192) in the contiguous and zigzag layouts: counted TFLOP/s of
+    the forward (4 d per visible pair) and of the backward (10 d)."""
+    out = {}
+    base = rs.workloads()["bwd_64k"]
+    for key, w in (("bwd_64k_contig", base),
+                   ("bwd_64k_zigzag", base.replace(name=base.name + "_zigzag", layout=rs.LAYOUT_ZIGZAG))):
+        ring = Ring(w, torch, ra, seed=w.cfg, with_bwd=True)
+        _, gpu_ms, f_ms, b_ms = time_ring(ring, steps, 1, True)
+        f_step, b_step = sum(f_ms) / steps, sum(b_ms) / steps
+        out[key] = {"fwd_ms": f_step, "bwd_ms": b_step,
+                    "fwd_tflops": counted_flops(w, 4) / (f_step / 1e3) / 1e12,
+                    "bwd_tflops": counted_flops(w, 10) / (b_step / 1e3) / 1e12,
+                    "gpu_event_ms_per_step": gpu_ms / steps}
+        del ring
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -429,6 +449,8 @@ def main():
         nc_rate = extra["fwd_kernel_tflops"]
         st = extra["causal"]["causal_256k_striped"]["tflops"]
         extra["striped_vs_noncausal_per_flop"] = st / nc_rate
+        log("[bench] causal 64K forward + backward")
+        extra["causal_bwd"] = bwd_rates(torch, ra)
         log("[bench] t_calc(c) sweep")
         extra["overlap"] = tcalc_sweep(torch, ra)
         log("[bench] finalize / merge bandwidth")

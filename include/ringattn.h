@@ -77,9 +77,10 @@ typedef enum { RA_MASK_NONE = 0, RA_MASK_CAUSAL = 1 } ra_mask_mode;
  * the sequence is cut into 2N chunks of c/2 tokens, host h holds chunk h in
  * rows 0..c/2-1 and chunk 2N-1-h in rows c/2..c-1, so every host sees the
  * same number of causal (query, key) pairs.  Zigzag needs an even block_len
- * (the scheduler and token index) and, in the ring forward, bf16 blocks with
- * block_len % 256 == 0; the backward and the block calls take contiguous or
- * striped only. */
+ * (the scheduler and token index) and, under the causal mask in the ring
+ * drivers, bf16 blocks with block_len % 256 == 0 (RA_ERR_UNSUPPORTED
+ * otherwise).  The block calls take one (q_offset, kv_offset, stride) triple
+ * and so serve zigzag blocks one quadrant at a time. */
 typedef enum { RA_LAYOUT_CONTIGUOUS = 0, RA_LAYOUT_STRIPED = 1, RA_LAYOUT_ZIGZAG = 2 } ra_layout;
 
 /* What a (query block, key block) pair needs under the mask.
@@ -272,7 +273,11 @@ ra_status ra_ring_workspace_size(const ra_ring_cfg *cfg, int32_t is_bwd, size_t 
  * half of its receive double buffer ([P1] 计算与通信重叠; [P3] 隐藏通信).
  * When all N hosts are simulated the copy is the ring send: host h's next
  * block is what host h-1 holds now.  After N steps ra_finalize runs on
- * `compute`.  stats (host pointer) may be NULL. */
+ * `compute`.  Work on `comm` is ordered after everything already queued on
+ * `compute` when the call is made (inputs produced there are safe to pass),
+ * and the call's last use of `comm` is ordered before its last work on
+ * `compute`, so synchronising `compute` covers the whole call.
+ * stats (host pointer) may be NULL. */
 ra_status ra_ring_fwd(const ra_ring_cfg *cfg, const void *Q, const void *K, const void *V,
                       void *O, float *lse, void *workspace, size_t workspace_bytes,
                       void *compute_stream, void *comm_stream, ra_ring_stats *stats);

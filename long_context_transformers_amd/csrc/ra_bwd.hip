@@ -87,11 +87,10 @@ void dkdv_kernel(BwdArgs a) {
   int logical = xcd_remap_b(blockIdx.x, gridDim.x);
   const int kt = logical % n_kt;
   logical /= n_kt;
+  const int host = logical % a.n_hosts;   // hosts next: every XCD gets a share of every host
+  logical /= a.n_hosts;
   const int kvh = logical % a.hkv;
-  logical /= a.hkv;
-  const int b = logical % a.batch;
-  const int host = logical / a.batch;
-  const int delta = a.delta[host];
+  const int b = logical / a.hkv;
   const int group = a.hq / a.hkv;
 
   const int tid = threadIdx.x;
@@ -129,19 +128,53 @@ void dkdv_kernel(BwdArgs a) {
         acc_dv[ks][nt][r] = 0.f;
       }
 
-  // queries that can see a key of this workgroup: q >= k0 - delta
-  const int q_start = max(0, k0 - delta);
-  const int qt0 = q_start / kTile;
-  const int n_qt = (q_start >= c) ? 0 : (c + kTile - 1) / kTile - qt0;
-  const int n_iter = n_qt * group;                         // (query head of the group, query tile)
+  // Query segments with one visibility offset each: the whole block, or, for
+  // a zigzag block (zz_half = c/2, a multiple of BK), the two query halves
+  // seen from this workgroup's key half.  Segment sg holds the query tiles
+  // [sq[sg], sq[sg] + nq[sg]) that can see a key of this workgroup
+  // (q >= k0 - delta), as iterations [ib[sg], ib[sg] + nq[sg] * group) of
+  // the (query tile, query head of the group) sweep; of these, [ib, iu) are
+  // masked (diagonal band), [iu, it) unmasked and [it, end) masked (ragged
+  // last tile).
+  const int zh = a.zz_half;
+  int sq[2], ib[3], iu[2], itl[2], sd[2];
+  ib[0] = 0;
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg) {
+    const int lo = zh ? sg * zh : 0, hi = zh ? lo + zh : c;
+    const int d = zh ? a.delta4[host][2 * sg + (k0 >= zh ? 1 : 0)] : a.delta[host];
+    const int q_start = max(lo, k0 - d);
+    const int qt0 = q_start / kTile;
+    const int n_qt = ((sg == 0 || zh) && q_start < hi) ? (hi + kTile - 1) / kTile - qt0 : 0;
+    const int n = n_qt * group;
+    int na = n, nb = n;                                  // masked head, end of the unmasked run
+    if (k0 + BK <= c) {
+      const int need = k0 + BK - 1 - d;                  // smallest fully visible q0
+      const int qt_full = need <= 0 ? 0 : (need + kTile - 1) / kTile;
+      na = min(n, max(0, qt_full - qt0) * group);
+      nb = max(na, n - ((hi % kTile) ? group : 0));
+    }
+    sq[sg] = qt0;
+    sd[sg] = d;
+    iu[sg] = ib[sg] + na;
+    itl[sg] = ib[sg] + nb;
+    ib[sg + 1] = ib[sg] + n;
+  }
+  const int n_iter = ib[2];
+  // iteration -> (first query row, query head of the group)
+  auto tile_of = [&](int it, int& q0, int& hg) {
+    const int sg = it >= ib[1] ? 1 : 0;
+    const int li = it - ib[sg];
+    hg = li % group;
+    q0 = (sq[sg] + li / group) * kTile;
+  };
 
-  // Tile `it` (query tile qt0 + it / group of query head kvh*group + it % group)
-  // goes to stage it % NS by LDS-DMA: Q and dO rows, and the 64 lse and D
-  // values (32 per wave: lse rows 0..31, 32..63 from waves 0, 1; D from
-  // waves 2, 3; lanes 0..7).  Rows past the block read as 0.
+  // Tile `it` goes to stage it % NS by LDS-DMA: Q and dO rows, and the 64
+  // lse and D values (32 per wave: lse rows 0..31, 32..63 from waves 0, 1;
+  // D from waves 2, 3; lanes 0..7).  Rows past the block read as 0.
   auto issue = [&](int it) {
-    const int hg = it % group;
-    const int q0 = (qt0 + it / group) * kTile;
+    int q0, hg;
+    tile_of(it, q0, hg);
     const int head = kvh * group + hg;
     const int64_t qoff = host * a.q_host_stride + ((int64_t)(b * a.hq + head) * c) * D;
     const __amdgpu_buffer_rsrc_t rq = rsrc(reinterpret_cast<const __bf16*>(a.q) + qoff, blk_bytes);
@@ -185,8 +218,10 @@ void dkdv_kernel(BwdArgs a) {
   //     four MFMAs.  P^T's item j of lane (g, i) is query 32kq + 16(j/4) +
   //     4g + j%4, the order in which the transposing reads deliver dO and Q.
   // Operand reads run kPre slots ahead, pinned by sched_barrier.
+  int delta = sd[0];                                       // the current segment's offset
   auto compute = [&](int it, auto masked) {
-    const int q0 = (qt0 + it / group) * kTile;
+    int q0, hg_unused;
+    tile_of(it, q0, hg_unused);
     const unsigned char* base = smem + (it % NS) * BUF;
     const unsigned char* qs = base;
     const unsigned char* os = base + T::BYTES;
@@ -280,7 +315,8 @@ void dkdv_kernel(BwdArgs a) {
     if (it + NS - 1 < n_iter) issue(it + NS - 1);        // into the stage read in iteration it - 1
     if constexpr (decltype(masked)::value) {
       // keys [kw0, kw0+32) against queries [q0, q0+64): skip when none is visible
-      const int q0 = (qt0 + it / group) * kTile;
+      int q0, hg_unused;
+      tile_of(it, q0, hg_unused);
       if ((kw0 < c) && visible(kw0 - (q0 + kTile - 1), delta)) compute(it, masked);
     } else {
       compute(it, masked);
@@ -294,21 +330,17 @@ void dkdv_kernel(BwdArgs a) {
     if (i < n_iter) issue(i);
   if (n_iter > 0) wait_tile(0, min(NS - 2, n_iter - 1));
   __syncthreads();
-  // Query tiles run in order (heads of the group innermost); tile qt needs no
+  // Query tiles run in order (heads of the group innermost); a tile needs no
   // per-element mask when every pair of this workgroup is visible and in
-  // range: qt >= qt_full (diagonal band above) and a complete tile.  Masked
-  // head, unmasked middle and masked tail run as separate loops so the
-  // accumulators keep their registers across iterations.
-  int it_a = n_iter, it_b = n_iter;
-  if (k0 + BK <= c) {
-    const int need = k0 + BK - 1 - delta;                   // smallest fully visible q0
-    const int qt_full = need <= 0 ? 0 : (need + kTile - 1) / kTile;
-    it_a = min(n_iter, max(0, qt_full - qt0) * group);
-    it_b = max(it_a, n_iter - ((c % kTile) ? group : 0));
+  // range.  Masked head, unmasked middle and masked tail of each segment run
+  // as separate loops so the accumulators keep their registers.
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg) {
+    delta = sd[sg];
+    for (int it = ib[sg]; it < iu[sg]; ++it) step(it, std::true_type{});
+    for (int it = iu[sg]; it < itl[sg]; ++it) step(it, std::false_type{});
+    for (int it = itl[sg]; it < ib[sg + 1]; ++it) step(it, std::true_type{});
   }
-  for (int it = 0; it < it_a; ++it) step(it, std::true_type{});
-  for (int it = it_a; it < it_b; ++it) step(it, std::false_type{});
-  for (int it = it_b; it < n_iter; ++it) step(it, std::true_type{});
 
   // epilogue: out = in + contribution (scale on dK).  The accumulators are
   // staged through the (idle) LDS stages as row-major fp32 [BK keys][D] for
@@ -384,11 +416,10 @@ void dq_kernel(BwdArgs a) {
   int logical = xcd_remap_b(blockIdx.x, gridDim.x);
   const int rt = n_rt - 1 - (logical % n_rt);
   logical /= n_rt;
+  const int host = logical % a.n_hosts;   // hosts next: every XCD gets a share of every host
+  logical /= a.n_hosts;
   const int hg = logical % n_hg;
-  logical /= n_hg;
-  const int b = logical % a.batch;
-  const int host = logical / a.batch;
-  const int delta = a.delta[host];
+  const int b = logical / n_hg;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -398,11 +429,29 @@ void dq_kernel(BwdArgs a) {
   const int q0 = rt * ROWS;
   const int qw0 = q0 + (wave % WPH) * 32;                  // this wave's rows: sub-tiles of 16
   const int row_last = min(q0 + ROWS, c) - 1;
-  const int kend = min(c, row_last + delta + 1);
-  const int ntiles = kend > 0 ? (kend + kTile - 1) / kTile : 0;
-  if (ntiles == 0 && a.dq_accumulate) return;              // nothing visible: dQ unchanged
-  int n_unmasked = min((delta + q0 - (kTile - 1)) >= 0 ? (delta + q0 - (kTile - 1)) / kTile + 1 : 0, c / kTile);
-  n_unmasked = min(n_unmasked, ntiles);
+  // Key segments with one visibility offset each: the whole block, or, for a
+  // zigzag block (zz_half = c/2, a multiple of ROWS and kTile), the two key
+  // halves seen from this row tile's query half.  Segment sg covers key
+  // tiles [sb, se): [sb, su) fully visible and complete (no mask), [su, se)
+  // masked.
+  const int zh = a.zz_half;
+  int sb[2], su[2], se[2], sd[2];
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg) {
+    const int lo = zh ? sg * zh : 0, hi = zh ? lo + zh : c;
+    const int d = zh ? a.delta4[host][2 * (q0 >= zh ? 1 : 0) + sg] : a.delta[host];
+    const int kend = min(hi, row_last + d + 1);           // keys [lo, kend) can be visible
+    const int tb = lo / kTile, te = kend > lo ? (kend + kTile - 1) / kTile : tb;
+    int tu = (d + q0 - (kTile - 1)) >= 0 ? (d + q0 - (kTile - 1)) / kTile + 1 : 0;
+    tu = max(tb, min(min(tu, c / kTile), te));
+    const bool used = (sg == 0 || zh) && te > tb;
+    sb[sg] = tb;
+    su[sg] = used ? tu : tb;
+    se[sg] = used ? te : tb;
+    sd[sg] = d;
+  }
+  const bool any_keys = se[0] > sb[0] || se[1] > sb[1];
+  if (!any_keys && a.dq_accumulate) return;                // nothing visible: dQ unchanged
   const int blk_bytes = c * D * 2;
 
   const int64_t qoff = host * a.q_host_stride + ((int64_t)(b * a.hq + head) * c) * D;
@@ -468,14 +517,17 @@ void dq_kernel(BwdArgs a) {
   //     v = (kq, nt) reads the transposed K operand and feeds two MFMAs.
   //     dS^T's item j of lane (g, i) is key 32kq + 16(j/4) + 4g + j%4, the
   //     order in which the transposing read delivers K.
-  auto step = [&](int t, auto masked) {
-    if (t + 1 < ntiles) {
-      unsigned char* nb = smem + ((t + 1) & 1) * BUF;
-      T::dma(rk, nb, (t + 1) * kTile, wave, lane);
-      TV::dma(rv, nb + T::BYTES, (t + 1) * kTile, wave, lane);
+  // tile t in LDS buffer `buf`; tile tn (-1: none) is prefetched into the
+  // other buffer; delta is the current segment's offset
+  int delta = sd[0];
+  auto step = [&](int t, int tn, int buf, auto masked) {
+    if (tn >= 0) {
+      unsigned char* nb = smem + (buf ^ 1) * BUF;
+      T::dma(rk, nb, tn * kTile, wave, lane);
+      TV::dma(rv, nb + T::BYTES, tn * kTile, wave, lane);
     }
     const int kb0 = t * kTile;
-    const unsigned char* ks_ = smem + (t & 1) * BUF;
+    const unsigned char* ks_ = smem + buf * BUF;
     const unsigned char* vs_ = ks_ + T::BYTES;
     constexpr int NU = 2 * NKK, NC = 2 * NT, kPre = 2;     // slots per half (A), per tile (C)
     bf16x8 dsb[2][2];                                      // [qs][kq]
@@ -544,14 +596,24 @@ void dq_kernel(BwdArgs a) {
     __syncthreads();
   };
 
-  if (ntiles > 0) {
-    T::dma(rk, smem, 0, wave, lane);
-    TV::dma(rv, smem + T::BYTES, 0, wave, lane);
+  if (any_keys) {
+    const int t_first = se[0] > sb[0] ? sb[0] : sb[1];
+    T::dma(rk, smem, t_first * kTile, wave, lane);
+    TV::dma(rv, smem + T::BYTES, t_first * kTile, wave, lane);
     dma_wait();
   }
   __syncthreads();
-  for (int t = 0; t < n_unmasked; ++t) step(t, std::false_type{});
-  for (int t = n_unmasked; t < ntiles; ++t) step(t, std::true_type{});
+  int buf = 0;
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg) {
+    if (se[sg] > sb[sg]) {
+      delta = sd[sg];
+      const int te = se[sg];
+      const int tnext = (sg == 0 && se[1] > sb[1]) ? sb[1] : -1;
+      for (int t = sb[sg]; t < su[sg]; ++t, buf ^= 1) step(t, t + 1 < te ? t + 1 : tnext, buf, std::false_type{});
+      for (int t = su[sg]; t < te; ++t, buf ^= 1) step(t, t + 1 < te ? t + 1 : tnext, buf, std::true_type{});
+    }
+  }
 
   const float scale = a.scale;
 #pragma unroll

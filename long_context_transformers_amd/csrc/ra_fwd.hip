@@ -96,10 +96,10 @@ void fwd_bf16_kernel(FwdArgs a) {
   int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int rt = n_rt - 1 - (logical % n_rt);
   logical /= n_rt;
+  const int host = logical % a.n_hosts;   // hosts next: every XCD gets a share of every host
+  logical /= a.n_hosts;
   const int hg = logical % n_hg;
-  logical /= n_hg;
-  const int b = logical % a.batch;
-  const int host = logical / a.batch;
+  const int b = logical / n_hg;
 
   const int q0 = rt * ROWS;
   const int row_last = min(q0 + ROWS, c) - 1;
@@ -373,10 +373,10 @@ void fwd_f32_kernel(FwdArgs a) {
   int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int rt = n_rt - 1 - (logical % n_rt);
   logical /= n_rt;
+  const int host = logical % a.n_hosts;   // hosts next: every XCD gets a share of every host
+  logical /= a.n_hosts;
   const int hg = logical % n_hg;
-  logical /= n_hg;
-  const int b = logical % a.batch;
-  const int host = logical / a.batch;
+  const int b = logical / n_hg;
   const int delta = a.delta[host];
   const int q0 = rt * ROWS;
   const int row_last = min(q0 + ROWS, c) - 1;

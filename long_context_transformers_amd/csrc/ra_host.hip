@@ -224,6 +224,16 @@ struct RingEvents {
     }
     return hipSuccess;
   }
+  // Order `comm` after the work already queued on `compute`: the first
+  // transfer reads K/V that the caller may have just produced on `compute`,
+  // and writes receive slot 1, which a previous call on the same workspace
+  // may still be reading there.  Later transfers wait on used[] per slot.
+  hipError_t order_comm_after_compute(hipStream_t compute, hipStream_t comm) {
+    if (comm == compute) return hipSuccess;
+    hipError_t e = hipEventRecord(used[1], compute);
+    if (e != hipSuccess) return e;
+    return hipStreamWaitEvent(comm, used[1], 0);
+  }
 };
 
 // Enqueue, on `comm`, the K/V transfers that fill receive slot (s+1)&1 for
@@ -500,6 +510,7 @@ ra_status ra_ring_fwd(const ra_ring_cfg* cfg, const void* Q, const void* K, cons
 
   RingEvents ev;
   RA_HIP(ev.create(), "event create");
+  RA_HIP(ev.order_comm_after_compute(cs, ms), "order comm after compute");
   RA_HIP(ra::launch_state_init(m, l, ost, na * q_rows(d), d->head_dim, cs), "state_init launch");
 
   std::vector<ra_step> sched((size_t)na * N);
@@ -571,8 +582,10 @@ ra_status ra_ring_bwd(const ra_ring_cfg* cfg, const void* Q, const void* K, cons
   RA_CHECK(check_cfg(cfg));
   if (cfg->host_begin != 0 || cfg->host_end != cfg->n_hosts)
     return fail(RA_ERR_UNSUPPORTED, "ring backward runs every host (host_begin = 0, host_end = n_hosts)");
-  if (cfg->layout == RA_LAYOUT_ZIGZAG)
-    return fail(RA_ERR_UNSUPPORTED, "ring backward takes contiguous or striped layouts");
+  const bool zz = cfg->layout == RA_LAYOUT_ZIGZAG && cfg->mask == RA_MASK_CAUSAL;
+  if (zz && cfg->dims.block_len % 256 != 0)
+    return fail(RA_ERR_UNSUPPORTED, "causal zigzag ring backward needs block_len %% 256 == 0 (got %d)",
+                cfg->dims.block_len);
   if (cfg->flags & RA_FLAG_ELIDE_SKIPPED_COPIES)
     return fail(RA_ERR_INVALID_ARG, "copy elision does not apply to the full ring");
   RA_CHECK(check_ptr(Q, "Q"));
@@ -608,6 +621,7 @@ ra_status ra_ring_bwd(const ra_ring_cfg* cfg, const void* Q, const void* K, cons
 
   RingEvents ev;
   RA_HIP(ev.create(), "event create");
+  RA_HIP(ev.order_comm_after_compute(cs, ms), "order comm after compute");
   RA_HIP(ra::launch_bwd_pre(O, dO, Dbuf, (int64_t)N * q_rows(d), d->head_dim, d->dtype, cs), "bwd_pre launch");
   st.kernel_launches++;
 
@@ -643,10 +657,16 @@ ra_status ra_ring_bwd(const ra_ring_cfg* cfg, const void* Q, const void* K, cons
     a.batch = d->batch; a.hq = d->heads_q; a.hkv = d->heads_kv; a.c = d->block_len; a.n_hosts = N;
     a.scale = eff_scale(d);
     a.scale_log2 = a.scale * kLog2e;
+    a.zz_half = zz ? d->block_len / 2 : 0;
     for (int h = 0; h < N; ++h) {
       ra_step stp;
       schedule_one(N, h, d->block_len, cfg->layout, cfg->mask, s, &stp);
-      a.delta[h] = compute_delta(cfg->mask, stp.q_offset, stp.kv_offset, stp.stride, d->block_len);
+      if (zz) {
+        a.delta[h] = d->block_len;
+        zz_delta4(cfg->mask, N, h, stp.src, d->block_len, a.delta4[h]);
+      } else {
+        a.delta[h] = compute_delta(cfg->mask, stp.q_offset, stp.kv_offset, stp.stride, d->block_len);
+      }
       if (stp.cls == RA_BLK_SKIP) st.skipped_blocks++;
     }
     if (cfg->step_events) RA_HIP(hipEventRecord((hipEvent_t)cfg->step_events[2 * s], cs), "record step event");

@@ -64,6 +64,8 @@ struct BwdArgs {
   float scale;
   float scale_log2;
   int32_t delta[kMaxHostsPerLaunch];
+  int32_t zz_half;                          // zigzag quadrant offsets, as in FwdArgs
+  int32_t delta4[kMaxHostsPerLaunch][4];
 };
 
 // Kernel launchers (defined in the .hip files).  Return the hipError_t of the launch.

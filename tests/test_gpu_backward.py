@@ -10,7 +10,7 @@ from oracle import cref
 from tests import gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
-C, S = rs.LAYOUT_CONTIGUOUS, rs.LAYOUT_STRIPED
+C, S, Z = rs.LAYOUT_CONTIGUOUS, rs.LAYOUT_STRIPED, rs.LAYOUT_ZIGZAG
 TOL_BWD = 2e-2
 
 
@@ -79,6 +79,11 @@ SMALL = [
     (2, 2, 128, S, 1, 4, 64),
     (2, 2, 64, C, 0, 2, 300),
     (4, 2, 64, S, 1, 3, 129),
+    (2, 2, 128, Z, 1, 3, 256),
+    (4, 2, 128, Z, 1, 4, 512),
+    (4, 1, 64, Z, 1, 2, 256),
+    (2, 2, 128, Z, 1, 1, 256),
+    (2, 2, 128, Z, 0, 3, 130),
 ]
 
 
@@ -134,9 +139,10 @@ def test_block_bwd_accumulates(torch):
     _compare("block_bwd dV", _gather(dV, rows), dVr)
 
 
-def test_ring_bwd_concurrent_equals_serialized(torch):
+@pytest.mark.parametrize("layout", [C, Z])
+def test_ring_bwd_concurrent_equals_serialized(torch, layout):
     import long_context_transformers_amd as ra
-    w = rs.Workload("bwd_race", 97, 1, 4, 4, 128, 8, 512, rs.DT_BF16, 1, C, 0, 8)
+    w = rs.Workload("bwd_race", 97, 1, 4, 4, 128, 8, 512, rs.DT_BF16, 1, layout, 0, 8)
     inp = rs.make_inputs(w, with_do=True)
     q, k, v, do = (H.dev_tensor(x, w.dtype) for x in (inp.q_dev, inp.k_dev, inp.v_dev, inp.do_dev))
     O, lse = _fwd(torch, w, q, k, v)
@@ -187,3 +193,31 @@ def test_ring_bwd_64k_causal(torch):
     _compare("ring_bwd bwd_64k dQ", _gather(dQ, rows), dQr)
     _compare("ring_bwd bwd_64k dK", _gather(dK, krows, heads), dKr)
     _compare("ring_bwd bwd_64k dV", _gather(dV, krows, heads), dVr)
+
+
+@pytest.mark.timeout(600)
+def test_ring_bwd_zigzag_mid_sampled(torch):
+    """Causal zigzag backward, 8 hosts x 2048 (each half spans 8 key tiles
+    of 128), 8 query heads on 4 KV heads, d = 128: dQ on 512 seeded rows of
+    every head, dK and dV on 512 seeded key rows of 2 seeded KV heads."""
+    import long_context_transformers_amd as ra
+    w = rs.Workload("bwd_zz_mid", 98, 1, 8, 4, 128, 8, 2048, rs.DT_BF16, 1, Z, 0, 8)
+    inp = H.inputs(w, with_do=True)
+    q, k, v, do = (H.dev_tensor(x, w.dtype) for x in (inp.q_dev, inp.k_dev, inp.v_dev, inp.do_dev))
+    O, lse = _fwd(torch, w, q, k, v)
+    cfg = H.cfg_of(w)
+    dQ = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    dK = torch.empty(k.shape, dtype=torch.float32, device="cuda")
+    dV = torch.empty(v.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(ra.ring_workspace_size(cfg, True), dtype=torch.uint8, device="cuda")
+    stats = ra.ring_bwd(cfg, q, k, v, O, lse, do, dQ, dK, dV, ws, torch.cuda.current_stream(),
+                        torch.cuda.Stream())
+    torch.cuda.synchronize()
+    assert stats["skipped_blocks"] == 0
+    rows = rs.row_sample(w, 512)
+    krows = rs.row_sample(w, 512, seed=9500 + w.cfg)
+    heads = [1, 3]
+    dQr, dKr, dVr = _oracle_grads(w, inp, rows, krows, heads)
+    _compare("ring_bwd zigzag mid dQ", _gather(dQ, rows), dQr)
+    _compare("ring_bwd zigzag mid dK", _gather(dK, krows, heads), dKr)
+    _compare("ring_bwd zigzag mid dV", _gather(dV, krows, heads), dVr)

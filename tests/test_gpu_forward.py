@@ -343,3 +343,44 @@ def test_ring_concurrent_equals_serialized(torch, layout, mask):
     t7 = (t[0][7:8].contiguous(), t[1], t[2])
     O4, l4, s4 = H.run_ring_fwd(w7, inp, tensors=t7, flags=ra.RA_FLAG_ELIDE_SKIPPED_COPIES)
     assert torch.equal(O4[0], O1[7]) and torch.equal(l4[0], l1[7])
+
+
+def test_ring_transfers_wait_for_inputs_on_compute_stream(torch):
+    """K and V produced on the compute stream just before the call (behind a
+    long matmul) reach the side-stream transfers intact: forward and backward
+    equal a run on inputs that were ready long before."""
+    import long_context_transformers_amd as ra
+    w = rs.Workload("order", 99, 1, 4, 2, 128, 4, 512, rs.DT_BF16, 1, C, 0, 4)
+    inp = rs.make_inputs(w, with_do=True)
+    q, k, v, do = (H.dev_tensor(x, w.dtype) for x in (inp.q_dev, inp.k_dev, inp.v_dev, inp.do_dev))
+    O1, l1, _ = H.run_ring_fwd(w, inp, tensors=(q, k, v))
+    k2, v2 = torch.zeros_like(k), torch.zeros_like(v)
+    a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    torch.cuda.synchronize()
+    for _ in range(8):
+        b = torch.matmul(a, a)                  # a few ms of work ahead of the copies below
+    k2.copy_(k)
+    v2.copy_(v)
+    O2, l2, _ = H.run_ring_fwd(w, inp, tensors=(q, k2, v2))
+    assert torch.equal(O1, O2) and torch.equal(l1, l2)
+    del b
+    cfg = H.cfg_of(w)
+    grads = []
+    for kk, vv in ((k, v), (None, None)):
+        if kk is None:
+            kk, vv = torch.zeros_like(k), torch.zeros_like(v)
+            torch.cuda.synchronize()
+            for _ in range(8):
+                b = torch.matmul(a, a)
+            kk.copy_(k)
+            vv.copy_(v)
+        dQ = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        dK = torch.empty(k.shape, dtype=torch.float32, device="cuda")
+        dV = torch.empty(v.shape, dtype=torch.float32, device="cuda")
+        ws = torch.empty(ra.ring_workspace_size(cfg, True), dtype=torch.uint8, device="cuda")
+        ra.ring_bwd(cfg, q, kk, vv, O1, l1, do, dQ, dK, dV, ws, torch.cuda.current_stream(),
+                    torch.cuda.Stream())
+        torch.cuda.synchronize()
+        grads.append((dQ, dK, dV))
+    for x, y in zip(*grads):
+        assert torch.equal(x, y)

@@ -226,11 +226,14 @@ def test_ring_argument_checks():
     assert _ring_fwd(_cfg(layout=Z, mask=1, dims=_dims(block_len=64)), big) == L.RA_ERR_UNSUPPORTED
     assert _ring_fwd(_cfg(layout=Z, mask=1, dims=_dims(block_len=256, dtype=1)), big) == L.RA_ERR_UNSUPPORTED
     st = L.RaRingStats()
-    # backward: partial host ranges and zigzag are not supported
+    # backward: partial host ranges, and causal zigzag with block_len % 256 != 0,
+    # are not supported
     assert ra.raw_call("ra_ring_bwd", ctypes.byref(_cfg(host_begin=7)), *([FAKE] * 10), 1 << 40,
                        None, None, ctypes.byref(st)) == L.RA_ERR_UNSUPPORTED
-    assert ra.raw_call("ra_ring_bwd", ctypes.byref(_cfg(layout=Z, dims=_dims(block_len=256))), *([FAKE] * 10),
-                       1 << 40, None, None, ctypes.byref(st)) == L.RA_ERR_UNSUPPORTED
+    assert ra.raw_call("ra_ring_bwd", ctypes.byref(_cfg(layout=Z, mask=1, dims=_dims(block_len=128))),
+                       *([FAKE] * 10), 1 << 40, None, None, ctypes.byref(st)) == L.RA_ERR_UNSUPPORTED
+    assert ra.raw_call("ra_ring_bwd", ctypes.byref(_cfg(layout=Z, dims=_dims(block_len=63))),
+                       *([FAKE] * 10), 1 << 40, None, None, ctypes.byref(st)) == L.RA_ERR_INVALID_ARG
 
 
 def test_workspace_size_formula():
