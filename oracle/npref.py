@@ -21,6 +21,10 @@ Functions and what they follow:
   dense_attention_grad -- closed-form gradient of dense_attention (the pages do not
                           print it; [P2] 5.2 only says dQ, dK, dV accumulate along
                           the ring).
+  decode_attention     -- [P2] 5.6 (Appendix C: autoregressive decoding with the KV
+                          cache spread over the ring) and [P3] 超长序列推理与KV Cache
+                          分发: one new query token per sequence attends to every
+                          valid cached key of every host's shard.
 
 Every function is pinned in tests/test_oracle_pins.py.
 """
@@ -230,3 +234,43 @@ def brute_force_row(q: Sequence[float], keys: Iterable[Sequence[float]],
         for e in range(d):
             out[e] += w * float(vv[e])
     return [o / total for o in out], mx + math.log(total)
+
+
+# ----------------------------------------------------------------------------
+# decoding against a ring-sharded KV cache
+# ----------------------------------------------------------------------------
+
+def decode_keys(x_hm: np.ndarray, lens: np.ndarray, b: int, kvh: int) -> np.ndarray:
+    """The valid cached rows of sequence b, KV head kvh, over all shards in
+    host order: x_hm [N][B][Hkv][c][d], lens [N][B] valid rows per shard."""
+    N = x_hm.shape[0]
+    return np.concatenate([x_hm[h, b, kvh, :int(lens[h][b])].astype(np.float64) for h in range(N)], axis=0)
+
+
+def decode_attention(q: np.ndarray, k_hm: np.ndarray, v_hm: np.ndarray, lens: np.ndarray,
+                     scale: float):
+    """One decode step ([P2] 5.6; [P3] KV-cache distribution over the ring):
+    q [B][Hq][d] holds each sequence's newest query token; the KV cache is
+    sharded over N hosts, host h holding lens[h][b] valid rows of sequence b.
+    The new token sees every cached key (all earlier tokens and its own, so
+    the causal mask removes nothing), so each (sequence, query head) is the
+    plain softmax(q K^T * scale) V over the valid keys of its KV head
+    (query head g uses KV head g // (Hq / Hkv)).  Returns O [B][Hq][d],
+    lse [B][Hq]; a sequence with no valid key gets O = 0, lse = -inf."""
+    B, Hq, d = q.shape
+    Hkv = k_hm.shape[2]
+    group = Hq // Hkv
+    O = np.zeros((B, Hq, d))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        for kvh in range(Hkv):
+            k = decode_keys(k_hm, lens, b, kvh)
+            v = decode_keys(v_hm, lens, b, kvh)
+            heads = slice(kvh * group, (kvh + 1) * group)
+            if k.shape[0] == 0:
+                continue
+            qq = q[b, heads].astype(np.float64)
+            o, l_, _, _ = dense_attention(qq, k, v, np.ones((group, k.shape[0]), dtype=bool), scale)
+            O[b, heads] = o
+            lse[b, heads] = l_
+    return O, lse

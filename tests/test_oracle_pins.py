@@ -470,3 +470,96 @@ def test_bf16_rounding_helper():
     assert back[2] == np.float32(1.0078125)
     assert back[0] == 1.0 and back[4] == 0.0
     assert abs(back[3] - x[3]) <= abs(x[3]) * 2 ** -8
+
+
+# ---------------------------------------------------------------------------
+# decoding against a ring-sharded KV cache ([P2] 5.6, [P3] KV-cache distribution)
+# ---------------------------------------------------------------------------
+
+def _decode_case(seed, N=3, B=2, Hq=4, Hkv=2, c=6, d=8):
+    q = _rand(seed, (B, Hq, d))
+    k = _rand(seed + 1, (N, B, Hkv, c, d))
+    v = _rand(seed + 2, (N, B, Hkv, c, d))
+    lens = np.random.default_rng(seed + 3).integers(0, c + 1, size=(N, B))
+    lens[0, 0] = 0
+    lens[N - 1, B - 1] = c
+    return q, k, v, lens
+
+
+def test_decode_vs_library_sdpa():
+    """Each (sequence, head) equals torch's fp64 SDPA with query length 1 over
+    the concatenated valid keys (a library routine, no mask)."""
+    import torch
+    q, k, v, lens = _decode_case(61)
+    scale = 8 ** -0.5
+    O, lse = npref.decode_attention(q, k, v, lens, scale)
+    B, Hq, d = q.shape
+    group = Hq // k.shape[2]
+    for b in range(B):
+        for hd in range(Hq):
+            kk = npref.decode_keys(k, lens, b, hd // group)
+            vv = npref.decode_keys(v, lens, b, hd // group)
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q[b, hd].astype(np.float64))[None, None], torch.from_numpy(kk)[None],
+                torch.from_numpy(vv)[None])
+            assert np.allclose(O[b, hd], ref[0, 0].numpy(), atol=1e-12, rtol=0)
+            s = (kk @ q[b, hd].astype(np.float64)) * scale
+            assert abs(lse[b, hd] - (s.max() + np.log(np.exp(s - s.max()).sum()))) < 1e-12
+
+
+def test_decode_vs_brute_force_and_causal_last_row():
+    """Pure-Python loops on a tiny case; and the decode of token S-1 equals the
+    last row of causal attention over the whole contiguous sequence."""
+    q, k, v, _ = _decode_case(71, N=2, B=1, Hq=2, Hkv=2, c=3, d=4)
+    N, c = k.shape[0], k.shape[3]
+    lens = np.full((N, 1), c)
+    scale = 0.5
+    O, lse = npref.decode_attention(q, k, v, lens, scale)
+    for hd in range(2):
+        keys = npref.decode_keys(k, lens, 0, hd)
+        vals = npref.decode_keys(v, lens, 0, hd)
+        ob, lb = npref.brute_force_row(q[0, hd], keys, vals, [True] * len(keys), scale)
+        assert np.allclose(O[0, hd], ob, atol=1e-13) and abs(lse[0, hd] - lb) < 1e-13
+    # whole-sequence view: replace the last token's query by q, causal row S-1
+    qs = _rand(72, (N, 1, 2, c, 4))
+    qs[N - 1, 0, :, c - 1] = q[0]
+    full = cref.attn_rows(qs, k, v, n_hosts=N, layout=C, causal=1,
+                          rows=cref.row_desc([N - 1], [0], [0, 1], [c - 1]), scale=scale)
+    assert np.allclose(full[0], O[0], atol=1e-12) and np.allclose(full[1], lse[0], atol=1e-12)
+
+
+def test_decode_closed_form_q_zero():
+    """Q = 0: every score is 0, so O is the mean of the valid V rows and
+    LSE = ln(number of valid keys)."""
+    q, k, v, lens = _decode_case(81)
+    O, lse = npref.decode_attention(np.zeros_like(q), k, v, lens, 0.3)
+    B, Hq = q.shape[:2]
+    group = Hq // k.shape[2]
+    for b in range(B):
+        n = int(lens[:, b].sum())
+        for hd in range(Hq):
+            vv = np.concatenate([v[h, b, hd // group, :lens[h, b]] for h in range(k.shape[0])])
+            assert np.allclose(O[b, hd], vv.mean(axis=0), atol=1e-13)
+            assert abs(lse[b, hd] - np.log(n)) < 1e-13
+
+
+def test_decode_shards_merge_in_any_order():
+    """The ring form: per-shard partials merged with the LSE merge, in any
+    host order, give the decode over all shards; an empty shard is neutral."""
+    q, k, v, lens = _decode_case(91, N=4)
+    scale = 8 ** -0.5
+    O, lse = npref.decode_attention(q, k, v, lens, scale)
+    N = k.shape[0]
+    parts = []
+    for h in range(N):
+        one = np.zeros_like(lens)
+        one[h] = lens[h]
+        parts.append(npref.decode_attention(q, k, v, one, scale))
+    for order in itertools.permutations(range(N)):
+        Om, lm = parts[order[0]]
+        for h in order[1:]:
+            Om, lm = npref.lse_merge(Om, lm, *parts[h])
+        assert np.allclose(Om, O, atol=1e-12) and np.allclose(lm, lse, atol=1e-12)
+    # a sequence with no valid key at all: O = 0, lse = -inf
+    Oz, lz = npref.decode_attention(q, k, v, np.zeros_like(lens), scale)
+    assert np.all(Oz == 0) and np.all(lz == -np.inf)
