@@ -370,6 +370,48 @@ def bwd_rates(torch, ra, steps=2):
     return out
 
 
+def decode_rates(torch, ra, reps=10):
+    """One decode step (ra_ring_decode) on the decode workloads: ms per step,
+    new tokens per second, and HBM GB/s counting the valid K and V rows read
+    once (the step's algorithmic bytes; q, the partials and O are < 0.01 %)
+    against the 8 TB/s peak.  Inputs are drawn on the device, seeded."""
+    out = {}
+    for key, w in rs.decode_workloads().items():
+        N, B, Hq, Hkv, d, c = w.n_hosts, w.batch, w.heads_q, w.heads_kv, w.head_dim, w.block_len
+        g = torch.Generator(device="cuda")
+        g.manual_seed(w.cfg)
+        k = torch.empty((N, B, Hkv, c, d), dtype=torch.bfloat16, device="cuda")
+        v = torch.empty_like(k)
+        for h in range(N):
+            k[h].normal_(generator=g)
+            v[h].normal_(generator=g)
+        q = torch.randn((B, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
+        lens = rs.decode_lens(N, B, c, w.cfg, full=True)
+        tl = torch.as_tensor(lens).cuda()
+        dims = ra.Dims(B, Hq, Hkv, d, c, rs.DT_BF16)
+        O = torch.empty((B, Hq, d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        ws = torch.empty(ra.decode_workspace_size(dims, N), dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            ra.ring_decode(dims, N, q, k, v, tl, O, lse, ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            ra.ring_decode(dims, N, q, k, v, tl, O, lse, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = int(lens.sum()) * Hkv * d * 2 * 2
+        out[key] = {"workload": w.name, "cache_tokens_per_seq": int(lens.sum() // B), "ms": ms,
+                    "tokens_per_s": B / (ms / 1e3), "GBs": nbytes / (ms / 1e3) / 1e9,
+                    "frac_hbm_peak": nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+                    "algorithmic_bytes": nbytes}
+        del k, v
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -379,6 +421,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only measure the decode workloads and print their JSON")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter scaling) and exit")
     args = ap.parse_args()
@@ -394,6 +438,9 @@ def main():
     ra.version()
     if args.copy_calibration:
         copy_calibration(torch, args.copy_calibration)
+        return
+    if args.decode_only:
+        print(json.dumps(decode_rates(torch, ra)), flush=True)
         return
 
     w = rs.workloads()["noncausal_32k"]
@@ -451,6 +498,8 @@ def main():
         extra["striped_vs_noncausal_per_flop"] = st / nc_rate
         log("[bench] causal 64K forward + backward")
         extra["causal_bwd"] = bwd_rates(torch, ra)
+        log("[bench] decode against a ring-sharded KV cache")
+        extra["decode"] = decode_rates(torch, ra)
         log("[bench] t_calc(c) sweep")
         extra["overlap"] = tcalc_sweep(torch, ra)
         log("[bench] finalize / merge bandwidth")

@@ -297,6 +297,44 @@ ra_status ra_ring_bwd(const ra_ring_cfg *cfg, const void *Q, const void *K, cons
                       void *comm_stream, ra_ring_stats *stats);
 
 /* ---------------------------------------------------------------------
+ * Decoding against a ring-sharded KV cache
+ * ------------------------------------------------------------------- */
+
+/* [P2] 5.6 (the paper's Appendix C) runs autoregressive decoding on the
+ * ring: the KV cache of a long context is spread over N hosts, one shard
+ * each, and the newest query token of each sequence meets every shard
+ * ([P3] 超长序列推理与KV Cache分发 describes the same split).  The new token
+ * sees every cached key, so the result is softmax(scale q K^T) V over all
+ * valid cached rows; each shard gives a partial (O, LSE) and the partials
+ * combine with the LogSumExp merge ([P1] Online Softmax).
+ *
+ * dims: batch B sequences, heads_q / heads_kv (at most 16 query heads per
+ *   KV head), head_dim 64 or 128, block_len c = rows per shard, dtype bf16
+ *   (RA_ERR_UNSUPPORTED otherwise), scale (0: 1/sqrt(d)).
+ * Workspace bytes for ra_ring_decode with n_hosts shards. */
+ra_status ra_decode_workspace_size(const ra_dims *dims, int32_t n_hosts, size_t *bytes);
+
+/* One decode step over n_hosts shards held on this GPU (all device pointers):
+ *   q:      [B][Hq][d] bf16, the newest token of each sequence
+ *   K, V:   [n_hosts][B][Hkv][c][d] bf16; shard h, sequence b holds
+ *           kv_len[h * B + b] valid rows (clamped to [0, c]) at rows
+ *           0 .. kv_len-1; rows past them are never read
+ *   kv_len: [n_hosts][B] int32, device memory (read by the kernels, so it may
+ *           change between calls without a host synchronisation)
+ *   O:      [B][Hq][d] out, o_dtype RA_BF16 or RA_F32
+ *   lse:    [B][Hq] fp32 out (natural log); a sequence with no valid row
+ *           gets O = 0, lse = -inf
+ *   workspace: >= ra_decode_workspace_size bytes, 256-byte aligned; holds
+ *           the per-chunk partials, which are merged in host order.
+ * Query head g uses KV head g / (Hq / Hkv).  With n_hosts = 1 and
+ * o_dtype = RA_F32 the call is one host's share; ra_merge_lse (dims with
+ * block_len = 1) combines such partials from several hosts.  Arguments are
+ * checked before any HIP call; the work is queued on `stream`. */
+ra_status ra_ring_decode(const ra_dims *dims, int32_t n_hosts, const void *q, const void *K,
+                         const void *V, const int32_t *kv_len, void *O, int32_t o_dtype, float *lse,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------
  * Errors and version
  * ------------------------------------------------------------------- */
 const char *ra_status_str(ra_status s);

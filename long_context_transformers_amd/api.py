@@ -188,6 +188,27 @@ def ring_bwd(cfg: RingCfg, q, k, v, O, lse, dO, dQ, dK, dV, workspace, compute_s
     return _stats(st)
 
 
+def decode_workspace_size(dims: Dims, n_hosts: int) -> int:
+    d = dims.c()
+    n = ctypes.c_size_t(0)
+    L.check(L.load().ra_decode_workspace_size(ctypes.byref(d), n_hosts, ctypes.byref(n)),
+            "ra_decode_workspace_size")
+    return int(n.value)
+
+
+def ring_decode(dims: Dims, n_hosts: int, q, k, v, kv_len, O, lse, workspace, o_dtype=None,
+                stream=None):
+    """One decode step over n_hosts KV-cache shards (ra_ring_decode); o_dtype
+    defaults to the dtype of O (bf16 or float32)."""
+    d = dims.c()
+    if o_dtype is None:
+        o_dtype = RA_BF16 if str(O.dtype) == "torch.bfloat16" else RA_F32
+    nbytes = workspace.numel() * workspace.element_size()
+    L.check(L.load().ra_ring_decode(ctypes.byref(d), n_hosts, _ptr(q), _ptr(k), _ptr(v), _ptr(kv_len),
+                                    _ptr(O), o_dtype, _ptr(lse), _ptr(workspace), nbytes,
+                                    _stream(stream)), "ra_ring_decode")
+
+
 def raw_call(name: str, *args) -> int:
     """Call an exported symbol directly (tests of argument checking)."""
     return int(getattr(L.load(), name)(*args))

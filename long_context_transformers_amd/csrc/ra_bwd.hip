@@ -23,9 +23,13 @@
 //  * dq_kernel owns query rows like the forward kernel (one query per lane):
 //    S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T with K^T from transposing
 //    reads of the row-major K tile.
-// Q/dO (dkdv) and K/V (dq) tiles travel HBM -> LDS by LDS-DMA buffer loads,
-// double buffered, into the swizzled row-major layout of ra_tile.h, which
-// serves both the row reads and the transposing reads without bank conflicts.
+// Q/dO (dkdv, a 4-stage ring) and K/V (dq, double buffered) tiles travel
+// HBM -> LDS by LDS-DMA buffer loads into the swizzled row-major layout of
+// ra_tile.h; a tile read both by rows and by transposing reads uses the
+// swizzle that keeps the transposing reads conflict-free (its row reads pay
+// a few extra cycles), a tile read only by rows the row-clean swizzle.
+// Zigzag blocks carry one offset per quadrant: dq_kernel sweeps the two key
+// halves, dkdv_kernel the two query halves, as separate segments.
 // The dK/dV result is written as (partial sum received) + (this block's
 // contribution) to an output location that may belong to another host: the
 // ring driver uses that to hand the running sum to the neighbour.

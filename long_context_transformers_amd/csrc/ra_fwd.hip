@@ -13,27 +13,32 @@
 // block (see ra_internal.h): tiles entirely above the band are skipped, tiles
 // crossing it are masked element by element, tiles below run unmasked.
 //
-// bf16 kernel design (wave64, MFMA 32x32x16 bf16 -> fp32):
-//  * A workgroup is 4 waves.  Each wave owns 32 query rows of one head; a
-//    workgroup covers 128 rows of one head, or 32 rows of 4 heads that share
-//    a key/value head (grouped heads), so one K/V tile in LDS feeds 4 heads.
-//  * Scores are computed transposed, S^T = K Q^T, so the MFMA result puts one
-//    query row per lane (lane % 32) and 16 of the 32 keys of an MFMA tile in
-//    that lane's registers; the other 16 keys sit in lane ^ 32.  Row max and
-//    row sum are then in-lane operations plus one cross-half exchange.
-//  * Q stays in registers for the whole block (B operand of S^T).  K tiles
-//    are staged row-major in LDS (A operand, 16-byte reads).  V tiles are
-//    staged transposed in LDS with the key order permuted within each group
-//    of 16, so the P^T fragment the score MFMA leaves in registers is directly
-//    the B operand of O^T += V^T P^T and every V^T operand is one 16-byte read.
-//  * LDS is double buffered: tile t+1 travels global -> registers while tile
-//    t is computed, and is written to the other LDS buffer afterwards; one
-//    barrier per tile.
-//  * exp is exp2 with log2(e) folded into the score scale; the state m is kept
+// bf16 kernel design (wave64, v_mfma_f32_16x16x32_bf16 -> fp32):
+//  * A workgroup is 4 waves, 2 workgroups per CU.  Each wave owns 32 query
+//    rows of one head as two 16-row sub-tiles; a workgroup covers 128 rows of
+//    one head, or 32 rows of up to 4 heads that share a key/value head
+//    (grouped heads), so one K/V tile in LDS feeds all of them.
+//  * Scores are computed transposed, S^T = K Q^T: the MFMA result puts one
+//    query row per lane column (lane % 16) and 4 keys per lane group, so the
+//    row max and row sum are in-lane over 16 keys plus two exchanges across
+//    the lane groups (v_permlane16_swap, v_permlane32_swap).
+//  * Q stays in registers for the whole block (B operand of S^T).  K and V
+//    tiles of 64 keys travel HBM -> LDS by LDS-DMA into unpadded, swizzled
+//    row-major tiles (ra_tile.h): K is read by rows (A operand of S^T), V by
+//    transposing reads (ds_read_b64_tr_b16), which deliver V^T in exactly
+//    the key order in which P^T sits in registers after the softmax, so P^T
+//    is directly the B operand of O^T += V^T P^T.
+//  * LDS is double buffered (tile t+1 is loaded while tile t is computed),
+//    one barrier per tile; masked and unmasked tiles run as separate loops.
+//  * Lazy rescaling: the reference max moves only when a row's max grows by
+//    more than a threshold; the state is re-referenced to the true max on
+//    exit.  exp is exp2 with log2(e) folded into the score scale; m is kept
 //    in natural-log units at the interface and in base 2 inside.
-//  * Workgroup ids are remapped so that the 8 XCDs each take a contiguous
-//    range of (host, head) tiles (their K/V stay in that XCD's L2), and row
-//    tiles run heaviest first (causal blocks: later rows see more keys).
+//  * Zigzag blocks (zz_half > 0) carry one offset per (query half, key half)
+//    quadrant; a row tile sweeps each key half as its own segment.
+//  * Workgroup ids are remapped so each XCD takes a contiguous range of
+//    tiles, with the host index right after the row tile (every XCD holds
+//    part of every host's work); row tiles run heaviest first.
 #include <type_traits>
 
 #include "ra_internal.h"

@@ -278,6 +278,45 @@ ra_status enqueue_transfer(const ra_ring_cfg* cfg, int s, const char* K, const c
 
 }  // namespace
 
+// Decode chunking: enough (host, sequence, KV head, chunk) workgroups to
+// fill the chip (about 2048), chunks a multiple of 128 keys.
+void decode_split(const ra_dims* d, int32_t n_hosts, int* n_split, int* chunk) {
+  const int64_t units = (int64_t)n_hosts * d->batch * d->heads_kv;
+  const int max_split = (d->block_len + 127) / 128;
+  const int64_t want = (2048 + units - 1) / units;
+  int ns = (int)std::max<int64_t>(1, std::min<int64_t>(max_split, want));
+  const int ch = ((d->block_len + ns - 1) / ns + 127) / 128 * 128;
+  ns = (d->block_len + ch - 1) / ch;
+  *n_split = ns;
+  *chunk = ch;
+}
+
+struct DecWs {
+  size_t m, l, o, total;
+};
+DecWs decode_ws(const ra_dims* d, int32_t n_hosts) {
+  int ns, ch;
+  decode_split(d, n_hosts, &ns, &ch);
+  const size_t parts = (size_t)n_hosts * d->batch * d->heads_q * ns;
+  DecWs w;
+  w.m = 0;
+  w.l = align256(parts * sizeof(float));
+  w.o = w.l + align256(parts * sizeof(float));
+  w.total = w.o + align256(parts * d->head_dim * sizeof(float));
+  return w;
+}
+
+ra_status check_decode(const ra_dims* d, int32_t n_hosts) {
+  RA_CHECK(check_dims(d));
+  if (n_hosts < 1 || n_hosts > (1 << 16)) return fail(RA_ERR_INVALID_ARG, "n_hosts %d out of range [1, 65536]", n_hosts);
+  if (d->dtype != RA_BF16) return fail(RA_ERR_UNSUPPORTED, "decode takes bf16 q, K, V");
+  if (d->heads_q / d->heads_kv > 16)
+    return fail(RA_ERR_UNSUPPORTED, "decode handles up to 16 query heads per KV head (got %d)", d->heads_q / d->heads_kv);
+  if ((int64_t)n_hosts * d->batch * d->heads_kv * ((d->block_len + 127) / 128) > 0x7fffffff)
+    return fail(RA_ERR_UNSUPPORTED, "decode grid too large");
+  return RA_OK;
+}
+
 extern "C" {
 
 const char* ra_status_str(ra_status s) {
@@ -462,6 +501,52 @@ ra_status ra_mask_tile(int64_t q_offset, int64_t kv_offset, int64_t stride, int3
   const int32_t c = rows > cols ? rows : cols;
   const int32_t delta = compute_delta(RA_MASK_CAUSAL, q_offset, kv_offset, stride, c);
   RA_HIP(ra::launch_mask_tile(delta, rows, cols, out_dev, (hipStream_t)stream), "mask_tile launch");
+  return RA_OK;
+}
+
+ra_status ra_decode_workspace_size(const ra_dims* dims, int32_t n_hosts, size_t* bytes) {
+  RA_CHECK(check_decode(dims, n_hosts));
+  if (!bytes) return fail(RA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = decode_ws(dims, n_hosts).total;
+  return RA_OK;
+}
+
+ra_status ra_ring_decode(const ra_dims* dims, int32_t n_hosts, const void* q, const void* K, const void* V,
+                         const int32_t* kv_len, void* O, int32_t o_dtype, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  RA_CHECK(check_decode(dims, n_hosts));
+  if (o_dtype != RA_BF16 && o_dtype != RA_F32) return fail(RA_ERR_INVALID_ARG, "unknown o_dtype %d", o_dtype);
+  RA_CHECK(check_ptr(q, "q"));
+  RA_CHECK(check_ptr(K, "K"));
+  RA_CHECK(check_ptr(V, "V"));
+  if (!kv_len) return fail(RA_ERR_INVALID_ARG, "kv_len is NULL");
+  if (reinterpret_cast<uintptr_t>(kv_len) & 3u) return fail(RA_ERR_INVALID_ARG, "kv_len is not 4-byte aligned");
+  RA_CHECK(check_ptr(O, "O"));
+  if (!lse) return fail(RA_ERR_INVALID_ARG, "lse is NULL");
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(RA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+  RA_CHECK(check_ptr(workspace, "workspace"));
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(RA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  const DecWs w = decode_ws(dims, n_hosts);
+  if (workspace_bytes < w.total)
+    return fail(RA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, w.total);
+  ra::DecArgs a{};
+  a.q = q;
+  a.k = K;
+  a.v = V;
+  a.kv_len = kv_len;
+  char* ws = static_cast<char*>(workspace);
+  a.part_m = reinterpret_cast<float*>(ws + w.m);
+  a.part_l = reinterpret_cast<float*>(ws + w.l);
+  a.part_o = reinterpret_cast<float*>(ws + w.o);
+  a.n_hosts = n_hosts;
+  a.batch = dims->batch;
+  a.hq = dims->heads_q;
+  a.hkv = dims->heads_kv;
+  a.c = dims->block_len;
+  decode_split(dims, n_hosts, &a.n_split, &a.chunk);
+  a.scale_log2 = eff_scale(dims) * kLog2e;
+  RA_HIP(ra::launch_decode(a, dims->head_dim, O, lse, o_dtype == RA_BF16 ? 0 : 1, (hipStream_t)stream),
+         "decode launch");
   return RA_OK;
 }
 

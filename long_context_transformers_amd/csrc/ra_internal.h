@@ -68,6 +68,20 @@ struct BwdArgs {
   int32_t delta4[kMaxHostsPerLaunch][4];
 };
 
+// Decode launch arguments: one query token per sequence against n_hosts
+// KV-cache shards of capacity c rows; kv_len[h * batch + b] valid rows.
+struct DecArgs {
+  const void* q;           // [batch][hq][d] bf16
+  const void* k;           // [n_hosts][batch][hkv][c][d] bf16
+  const void* v;
+  const int32_t* kv_len;   // device [n_hosts][batch]
+  float* part_m;           // [n_hosts][batch][hq][n_split], natural-log units
+  float* part_l;
+  float* part_o;           // [n_hosts][batch][hq][n_split][d], referenced to part_m
+  int32_t n_hosts, batch, hq, hkv, c, n_split, chunk;   // chunk: keys per split, multiple of 128
+  float scale_log2;
+};
+
 // Kernel launchers (defined in the .hip files).  Return the hipError_t of the launch.
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, int dtype, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, int head_dim, int dtype, hipStream_t s);
@@ -83,5 +97,7 @@ hipError_t launch_permute(const void* src, void* dst, int batch, int heads, int 
 hipError_t launch_mask_tile(int delta, int rows, int cols, uint8_t* out, hipStream_t s);
 hipError_t launch_spin(uint64_t cycles, hipStream_t s);
 hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
+// decode split + combine; out [batch][hq][d] in out_dtype (0 bf16, 1 fp32), lse [batch][hq]
+hipError_t launch_decode(const DecArgs& a, int head_dim, void* out, float* lse, int out_dtype, hipStream_t s);
 
 }  // namespace ra

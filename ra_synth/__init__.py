@@ -203,3 +203,50 @@ def row_sample(w: Workload, n_rows: int = 1024, seed: Optional[int] = None) -> n
         if int(p) not in fixed:
             rows.append(int(p))
     return np.array(sorted(rows), dtype=np.int64)
+
+
+# ----------------------------------------------------------------------------
+# decoding against a ring-sharded KV cache
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """One decode step: `batch` sequences, each with one new query token,
+    against a KV cache sharded over `n_hosts` shards of `block_len` rows."""
+    name: str
+    cfg: int
+    batch: int
+    heads_q: int
+    heads_kv: int
+    head_dim: int
+    n_hosts: int
+    block_len: int
+
+    @property
+    def capacity(self) -> int:
+        return self.n_hosts * self.block_len
+
+
+def decode_workloads() -> dict:
+    """The decode shapes.  decode_8m follows the pages' inference example
+    (a 7B model with 32 heads of d = 128 served from 32 hosts): 32 shards of
+    256K rows, an 8M-token cache; decode_512k_gqa is a grouped-head case small
+    enough for the oracle to read every key."""
+    return {
+        "decode_8m": DecodeWorkload("decode_8m_H32_d128_N32_c262144", 20, 1, 32, 32, 128, 32, 262144),
+        "decode_512k_gqa": DecodeWorkload("decode_512k_Hq32_Hkv8_N8_c65536_B2", 21, 2, 32, 8, 128, 8, 65536),
+    }
+
+
+def decode_lens(n_hosts: int, batch: int, block_len: int, seed: int, full: bool = True) -> np.ndarray:
+    """Valid rows per shard, int32 [n_hosts][batch], for contiguous sharding
+    of each sequence's tokens: sequence b of length T_b puts tokens
+    [h c, (h+1) c) on shard h.  full=True draws T_b in ((N-1) c, N c] (every
+    shard but the last one full, as in a long-context server); full=False
+    draws T_b in [0, N c] (ragged, empty shards and sequences included)."""
+    rng = np.random.default_rng(seed)
+    cap = n_hosts * block_len
+    lo = (n_hosts - 1) * block_len + 1 if full else 0
+    T = rng.integers(lo, cap + 1, size=batch)
+    h = np.arange(n_hosts)[:, None]
+    return np.clip(T[None, :] - h * block_len, 0, block_len).astype(np.int32)

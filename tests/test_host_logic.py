@@ -283,3 +283,30 @@ def test_bench_pair_count_matches_oracle_masks():
                 for h in range(N):
                     want = sum(int(cref.block_mask(layout, mask, N, c, h, j).sum()) for j in range(N))
                     assert bench.counted_pairs(w, h) == want, (layout, mask, N, c, h)
+
+
+def test_decode_argument_checks():
+    """ra_ring_decode rejects bad arguments before any HIP call."""
+    d = _dims(batch=2, heads_q=8, heads_kv=2, block_len=1000)
+    n = ctypes.c_size_t(0)
+    assert ra.raw_call("ra_decode_workspace_size", ctypes.byref(d), 4, ctypes.byref(n)) == L.RA_OK
+    ws = n.value
+    assert ws >= 4 * 2 * 8 * (2 + 128) * 4
+    big = 1 << 40
+
+    def call(dims=d, nh=4, q=FAKE, k=FAKE, v=FAKE, lens=FAKE, o=FAKE, odt=0, lse=FAKE, w=FAKE, wb=big):
+        return ra.raw_call("ra_ring_decode", ctypes.byref(dims), nh, q, k, v, lens, o, odt, lse, w, wb, None)
+
+    assert call(dims=_dims(batch=2, heads_q=8, heads_kv=2, block_len=1000, dtype=1)) == L.RA_ERR_UNSUPPORTED
+    assert call(dims=_dims(heads_q=32, heads_kv=1)) == L.RA_ERR_UNSUPPORTED
+    assert call(dims=_dims(head_dim=96)) == L.RA_ERR_UNSUPPORTED
+    assert call(nh=0) == L.RA_ERR_INVALID_ARG
+    assert call(lens=None) == L.RA_ERR_INVALID_ARG
+    assert call(lens=FAKE + 2) == L.RA_ERR_INVALID_ARG
+    assert call(q=None) == L.RA_ERR_INVALID_ARG
+    assert call(odt=5) == L.RA_ERR_INVALID_ARG
+    assert call(lse=None) == L.RA_ERR_INVALID_ARG
+    assert call(w=FAKE + 16) == L.RA_ERR_INVALID_ARG
+    assert call(wb=ws - 1) == L.RA_ERR_WORKSPACE
+    assert ra.raw_call("ra_decode_workspace_size", ctypes.byref(d), 0, ctypes.byref(n)) == L.RA_ERR_INVALID_ARG
+    assert ra.raw_call("ra_decode_workspace_size", ctypes.byref(d), 4, None) == L.RA_ERR_INVALID_ARG
