@@ -21,6 +21,10 @@ Functions and what they follow:
   dense_attention_grad -- closed-form gradient of dense_attention (the pages do not
                           print it; [P2] 5.2 only says dQ, dK, dV accumulate along
                           the ring).
+  blockwise_ffn        -- [P2] 2 and 5.2-5.3 (the Blockwise Parallel Transformer's
+                          feedforward acts on the local block only, so its
+                          activation stays within 2bch): Y = GELU(X W1^T) W2^T per
+                          token, evaluated block by block.
   decode_attention     -- [P2] 5.6 (Appendix C: autoregressive decoding with the KV
                           cache spread over the ring) and [P3] 超长序列推理与KV Cache
                           分发: one new query token per sequence attends to every
@@ -274,3 +278,35 @@ def decode_attention(q: np.ndarray, k_hm: np.ndarray, v_hm: np.ndarray, lens: np
             O[b, heads] = o
             lse[b, heads] = l_
     return O, lse
+
+
+# ----------------------------------------------------------------------------
+# the blockwise feedforward of the local block
+# ----------------------------------------------------------------------------
+
+def gelu(x: np.ndarray) -> np.ndarray:
+    """GELU with the exact Gaussian CDF: x * Phi(x) = x (1 + erf(x / sqrt 2)) / 2."""
+    from scipy.special import erf
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
+
+
+def blockwise_ffn(x: np.ndarray, w1: np.ndarray, w2: np.ndarray, block_rows: Optional[int] = None):
+    """Feedforward of a block of tokens ([P2] 2 and 5.2-5.3: it acts on each
+    token of the local block alone, so the layer's activation stays within
+    2bch when it is evaluated block by block).  The pages do not fix the
+    network; the reading is the standard two-layer feedforward with GELU:
+    Y = GELU(X W1^T) W2^T, x [rows][h], w1 [f][h], w2 [h][f] (the weights of
+    two linear layers, out-features major).  ``block_rows`` evaluates the
+    rows in blocks of that size, as a blockwise schedule would; the result
+    does not depend on it."""
+    x = np.asarray(x, dtype=np.float64)
+    w1 = np.asarray(w1, dtype=np.float64)
+    w2 = np.asarray(w2, dtype=np.float64)
+    n = x.shape[0]
+    step = n if not block_rows else block_rows
+    out = np.empty((n, w2.shape[0]))
+    for r0 in range(0, n, max(step, 1)):
+        hblk = gelu(x[r0:r0 + step] @ w1.T)
+        out[r0:r0 + step] = hblk @ w2.T
+    return out

@@ -563,3 +563,49 @@ def test_decode_shards_merge_in_any_order():
     # a sequence with no valid key at all: O = 0, lse = -inf
     Oz, lz = npref.decode_attention(q, k, v, np.zeros_like(lens), scale)
     assert np.all(Oz == 0) and np.all(lz == -np.inf)
+
+
+# ---------------------------------------------------------------------------
+# blockwise feedforward ([P2] 2, 5.2-5.3)
+# ---------------------------------------------------------------------------
+
+def test_gelu_vs_math_erf_and_torch():
+    import torch
+    x = np.concatenate([np.linspace(-9, 9, 181), _rand(101, (50,)).astype(np.float64) * 3])
+    g = npref.gelu(x)
+    loops = np.array([0.5 * v * (1 + math.erf(v / math.sqrt(2))) for v in x])
+    assert np.allclose(g, loops, atol=1e-15, rtol=1e-14)
+    t = torch.nn.functional.gelu(torch.from_numpy(x), approximate="none").numpy()
+    assert np.allclose(g, t, atol=1e-15, rtol=1e-14)
+    assert npref.gelu(np.array([0.0]))[0] == 0.0
+
+
+def test_ffn_brute_force_and_identity():
+    """Pure-Python loops on a tiny case; identity weights reduce the
+    feedforward to the elementwise GELU."""
+    x = _rand(111, (3, 4)).astype(np.float64)
+    w1 = _rand(112, (5, 4)).astype(np.float64)
+    w2 = _rand(113, (4, 5)).astype(np.float64)
+    y = npref.blockwise_ffn(x, w1, w2)
+    for r in range(3):
+        hid = []
+        for j in range(5):
+            acc = sum(float(x[r, k]) * float(w1[j, k]) for k in range(4))
+            hid.append(0.5 * acc * (1 + math.erf(acc / math.sqrt(2))))
+        for i in range(4):
+            assert abs(y[r, i] - sum(hid[j] * float(w2[i, j]) for j in range(5))) < 1e-13
+    eye = np.eye(4)
+    assert np.allclose(npref.blockwise_ffn(x, eye, eye), npref.gelu(x), atol=1e-15)
+
+
+def test_ffn_is_per_token():
+    """Blocks of any size give the same result, and permuting the tokens
+    permutes the output: the feedforward never mixes tokens."""
+    x = _rand(121, (37, 16)).astype(np.float64)
+    w1 = _rand(122, (24, 16)).astype(np.float64) * 0.25
+    w2 = _rand(123, (16, 24)).astype(np.float64) * 0.25
+    y = npref.blockwise_ffn(x, w1, w2)
+    for b in (1, 5, 16, 37, 64):
+        assert np.allclose(npref.blockwise_ffn(x, w1, w2, block_rows=b), y, atol=1e-13)
+    perm = np.random.default_rng(124).permutation(37)
+    assert np.allclose(npref.blockwise_ffn(x[perm], w1, w2), y[perm], atol=1e-13)
