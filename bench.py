@@ -296,7 +296,7 @@ def causal_rates(torch, ra, steps=3):
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "ring_bwd_step_noncausal_32k_hbm_traffic.md")
 BWD_SOURCES = [os.path.join(ROOT, "long_context_transformers_amd", "csrc", n)
-               for n in ("ra_bwd.hip", "ra_tile.h", "ra_internal.h")]
+               for n in ("ra_bwd.hip", "ra_tile.h")]   # the backward kernels' code
 
 
 def bwd_sources_sha256():
@@ -412,6 +412,43 @@ def decode_rates(torch, ra, reps=10):
     return out
 
 
+def ffn_rates(torch, ra, reps=10):
+    """Blockwise feedforward (ra_block_ffn) of one host's block: TFLOP/s
+    counting the two products (4 rows h f), beside torch.matmul (hipBLASLt)
+    running the same two products with torch's GELU between them."""
+    out = {}
+    for key, w in rs.ffn_workloads().items():
+        g = torch.Generator(device="cuda")
+        g.manual_seed(w.cfg)
+        x = torch.randn((w.rows, w.h), generator=g, device="cuda").to(torch.bfloat16)
+        w1 = (torch.randn((w.f, w.h), generator=g, device="cuda") * w.h ** -0.5).to(torch.bfloat16)
+        w2 = (torch.randn((w.h, w.f), generator=g, device="cuda") * w.f ** -0.5).to(torch.bfloat16)
+        y = torch.empty_like(x)
+        ws = torch.empty(ra.ffn_workspace_size(w.block_rows, w.f), dtype=torch.uint8, device="cuda")
+        flops = 4.0 * w.rows * w.h * w.f
+
+        def timed(fn):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        ms = timed(lambda: ra.block_ffn(x, w1, w2, y, w.block_rows, ws))
+        w1t, w2t = w1.t().contiguous(), w2.t().contiguous()
+        ms_ref = timed(lambda: torch.matmul(torch.nn.functional.gelu(torch.matmul(x, w1t)), w2t))
+        out[key] = {"workload": w.name, "ms": ms, "tflops": flops / (ms / 1e3) / 1e12,
+                    "torch_matmul_ms": ms_ref, "torch_matmul_tflops": flops / (ms_ref / 1e3) / 1e12}
+        del x, w1, w2, y, ws, w1t, w2t
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -421,6 +458,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--ffn-only", action="store_true",
+                    help="only measure the blockwise feedforward and print its JSON")
     ap.add_argument("--decode-only", action="store_true",
                     help="only measure the decode workloads and print their JSON")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -441,6 +480,9 @@ def main():
         return
     if args.decode_only:
         print(json.dumps(decode_rates(torch, ra)), flush=True)
+        return
+    if args.ffn_only:
+        print(json.dumps(ffn_rates(torch, ra)), flush=True)
         return
 
     w = rs.workloads()["noncausal_32k"]
@@ -500,6 +542,8 @@ def main():
         extra["causal_bwd"] = bwd_rates(torch, ra)
         log("[bench] decode against a ring-sharded KV cache")
         extra["decode"] = decode_rates(torch, ra)
+        log("[bench] blockwise feedforward")
+        extra["ffn"] = ffn_rates(torch, ra)
         log("[bench] t_calc(c) sweep")
         extra["overlap"] = tcalc_sweep(torch, ra)
         log("[bench] finalize / merge bandwidth")

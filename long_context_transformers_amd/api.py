@@ -209,6 +209,22 @@ def ring_decode(dims: Dims, n_hosts: int, q, k, v, kv_len, O, lse, workspace, o_
                                     _stream(stream)), "ra_ring_decode")
 
 
+def ffn_workspace_size(block_rows: int, f: int) -> int:
+    n = ctypes.c_size_t(0)
+    L.check(L.load().ra_ffn_workspace_size(block_rows, f, ctypes.byref(n)), "ra_ffn_workspace_size")
+    return int(n.value)
+
+
+def block_ffn(X, W1, W2, Y, block_rows: int, workspace, stream=None):
+    """Blockwise feedforward Y = GELU(X W1^T) W2^T of [rows][h] bf16 X
+    (ra_block_ffn); W1 [f][h], W2 [h][f]."""
+    rows, h = X.shape[-2], X.shape[-1]
+    f = W1.shape[0]
+    nbytes = workspace.numel() * workspace.element_size()
+    L.check(L.load().ra_block_ffn(_ptr(X), _ptr(W1), _ptr(W2), _ptr(Y), X.numel() // h, h, f, block_rows,
+                                  _ptr(workspace), nbytes, _stream(stream)), "ra_block_ffn")
+
+
 def raw_call(name: str, *args) -> int:
     """Call an exported symbol directly (tests of argument checking)."""
     return int(getattr(L.load(), name)(*args))

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libringattn.so")
-SOURCES = ["ra_host.hip", "ra_fwd.hip", "ra_bwd.hip", "ra_elem.hip", "ra_decode.hip"]
+SOURCES = ["ra_host.hip", "ra_fwd.hip", "ra_bwd.hip", "ra_elem.hip", "ra_decode.hip", "ra_ffn.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

@@ -250,3 +250,26 @@ def decode_lens(n_hosts: int, batch: int, block_len: int, seed: int, full: bool 
     T = rng.integers(lo, cap + 1, size=batch)
     h = np.arange(n_hosts)[:, None]
     return np.clip(T[None, :] - h * block_len, 0, block_len).astype(np.int32)
+
+
+# ----------------------------------------------------------------------------
+# the blockwise feedforward of the local block
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class FfnWorkload:
+    """Feedforward of one host's block: `rows` tokens of width h, hidden f,
+    evaluated in row blocks of `block_rows`."""
+    name: str
+    cfg: int
+    rows: int
+    h: int
+    f: int
+    block_rows: int
+
+
+def ffn_workloads() -> dict:
+    """ffn_7b_c4096: a 7B-like layer (h = 4096, f = 4h) on one host's block of
+    4096 tokens (the block size of the non-causal 32K ring), evaluated as one
+    row block (the host's block is the unit of the blockwise schedule)."""
+    return {"ffn_7b_c4096": FfnWorkload("ffn_7b_h4096_f16384_c4096", 30, 4096, 4096, 16384, 4096)}

@@ -310,3 +310,26 @@ def test_decode_argument_checks():
     assert call(wb=ws - 1) == L.RA_ERR_WORKSPACE
     assert ra.raw_call("ra_decode_workspace_size", ctypes.byref(d), 0, ctypes.byref(n)) == L.RA_ERR_INVALID_ARG
     assert ra.raw_call("ra_decode_workspace_size", ctypes.byref(d), 4, None) == L.RA_ERR_INVALID_ARG
+
+
+def test_ffn_argument_checks():
+    """ra_block_ffn rejects bad arguments before any HIP call."""
+    n = ctypes.c_size_t(0)
+    assert ra.raw_call("ra_ffn_workspace_size", 256, 512, ctypes.byref(n)) == L.RA_OK
+    assert n.value == 256 * 512 * 2
+    assert ra.raw_call("ra_ffn_workspace_size", 256, 500, ctypes.byref(n)) == L.RA_ERR_INVALID_ARG
+    assert ra.raw_call("ra_ffn_workspace_size", 0, 512, ctypes.byref(n)) == L.RA_ERR_INVALID_ARG
+    big = 1 << 40
+
+    def call(x=FAKE, w1=FAKE, w2=FAKE, y=FAKE, rows=100, h=128, f=256, br=64, w=FAKE, wb=big):
+        return ra.raw_call("ra_block_ffn", x, w1, w2, y, rows, h, f, br, w, wb, None)
+
+    assert call(h=100) == L.RA_ERR_INVALID_ARG
+    assert call(f=0) == L.RA_ERR_INVALID_ARG
+    assert call(rows=-1) == L.RA_ERR_INVALID_ARG
+    assert call(br=0) == L.RA_ERR_INVALID_ARG
+    assert call(x=None) == L.RA_ERR_INVALID_ARG
+    assert call(w2=FAKE + 2) == L.RA_ERR_INVALID_ARG
+    assert call(w=FAKE + 64) == L.RA_ERR_INVALID_ARG
+    assert call(wb=64 * 256 * 2 - 1) == L.RA_ERR_WORKSPACE
+    assert call(h=65536, f=65536) == L.RA_ERR_UNSUPPORTED
