@@ -424,7 +424,7 @@ def ffn_rates(torch, ra, reps=10):
         w1 = (torch.randn((w.f, w.h), generator=g, device="cuda") * w.h ** -0.5).to(torch.bfloat16)
         w2 = (torch.randn((w.h, w.f), generator=g, device="cuda") * w.f ** -0.5).to(torch.bfloat16)
         y = torch.empty_like(x)
-        ws = torch.empty(ra.ffn_workspace_size(w.block_rows, w.f), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(ra.ffn_workspace_size(w.block_rows, w.h, w.f), dtype=torch.uint8, device="cuda")
         flops = 4.0 * w.rows * w.h * w.f
 
         def timed(fn):

@@ -345,12 +345,13 @@ ra_status ra_ring_decode(const ra_dims *dims, int32_t n_hosts, const void *q, co
  *   Y = GELU(X W1^T) W2^T   (GELU with the exact Gaussian CDF),
  * computed over row blocks of `block_rows` rows; the GELU output of one row
  * block ([block_rows][f] bf16) is the only intermediate and lives in the
- * caller's workspace.  All device pointers, bf16, row-major:
+ * caller's workspace, beside fp32 split-K partial sums when a row block is
+ * too small to give every CU a tile (ra_ffn_workspace_size covers both).  All device pointers, bf16, row-major:
  *   X [rows][h], W1 [f][h], W2 [h][f] (two linear layers' weights,
  *   out-features major), Y [rows][h] out.  h and f are multiples of 64.
  * Products accumulate in fp32; the GELU output is rounded to bf16 before
  * the second layer.  Arguments are checked before any HIP call. */
-ra_status ra_ffn_workspace_size(int64_t block_rows, int32_t f, size_t *bytes);
+ra_status ra_ffn_workspace_size(int64_t block_rows, int32_t h, int32_t f, size_t *bytes);
 ra_status ra_block_ffn(const void *X, const void *W1, const void *W2, void *Y, int64_t rows, int32_t h,
                        int32_t f, int64_t block_rows, void *workspace, size_t workspace_bytes,
                        void *stream);

@@ -209,9 +209,9 @@ def ring_decode(dims: Dims, n_hosts: int, q, k, v, kv_len, O, lse, workspace, o_
                                     _stream(stream)), "ra_ring_decode")
 
 
-def ffn_workspace_size(block_rows: int, f: int) -> int:
+def ffn_workspace_size(block_rows: int, h: int, f: int) -> int:
     n = ctypes.c_size_t(0)
-    L.check(L.load().ra_ffn_workspace_size(block_rows, f, ctypes.byref(n)), "ra_ffn_workspace_size")
+    L.check(L.load().ra_ffn_workspace_size(block_rows, h, f, ctypes.byref(n)), "ra_ffn_workspace_size")
     return int(n.value)
 
 

@@ -21,7 +21,14 @@
 //    buffered, and both operands are 16-byte row reads (contiguous in K), so
 //    no transposing reads are needed;
 //  * rows past M or N read as zeros (buffer range) and are not stored;
-//  * the epilogue applies GELU to the fp32 accumulators before rounding.
+//  * the epilogue applies GELU to the fp32 accumulators before rounding;
+//  * when the tile grid would leave CUs idle (fewer than 256 tiles), K is
+//    split over up to 8 workgroups per tile, each writing an fp32 partial,
+//    and gemm_splitk_reduce_kernel sums the partials in split order and
+//    applies the epilogue.
+#include <algorithm>
+#include <cstdint>
+
 #include "ra_internal.h"
 #include "ra_tile.h"
 
@@ -75,13 +82,18 @@ __device__ inline void tile_of_g(int L, int n_mb, int n_nb, int& mb, int& nb) {
 
 }  // namespace
 
+// splits > 1: workgroup blockIdx.x = z * tiles + L computes K range z of
+// tile L and writes fp32 partial sums to part[z][M][N] (no epilogue).
 template <bool GELU>
 __global__ __launch_bounds__(512) void gemm_nt_kernel(const __bf16* __restrict__ A, const __bf16* __restrict__ B,
-                                                      __bf16* __restrict__ Cout, int M, int N, int K) {
+                                                      __bf16* __restrict__ Cout, float* __restrict__ part, int M, int N,
+                                                      int K, int splits) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStage];
   const int n_mb = (M + kBM - 1) / kBM, n_nb = (N + kBN - 1) / kBN;
+  const int tiles = n_mb * n_nb;
+  const int z = blockIdx.x / tiles;
   int mb, nb;
-  tile_of_g(blockIdx.x, n_mb, n_nb, mb, nb);
+  tile_of_g(blockIdx.x % tiles, n_mb, n_nb, mb, nb);
   const int m0 = mb * kBM, n0 = nb * kBN;
 
   const int tid = threadIdx.x;
@@ -114,12 +126,13 @@ __global__ __launch_bounds__(512) void gemm_nt_kernel(const __bf16* __restrict__
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) roff[kk] = l16 * kRowB + (((4 * kk + g) ^ fswz(l16)) * 16);
 
-  const int n_k = K / kBK;
-  issue(0, 0);
+  const int n_k = K / kBK / splits;                          // K steps of this split
+  const int kt0 = z * n_k;
+  issue(kt0, 0);
   tile::dma_wait();
   __syncthreads();
   for (int kt = 0; kt < n_k; ++kt) {
-    if (kt + 1 < n_k) issue(kt + 1, (kt + 1) & 1);
+    if (kt + 1 < n_k) issue(kt0 + kt + 1, (kt + 1) & 1);
     const unsigned char* st = smem + (kt & 1) * kStage;
     const unsigned char* as = st + wm * kSlab;                 // this wave's 64 rows of A
     const unsigned char* bs = st + (4 + 2 * wn) * kSlab;       // this wave's 128 rows of B
@@ -151,24 +164,83 @@ __global__ __launch_bounds__(512) void gemm_nt_kernel(const __bf16* __restrict__
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         const int n = n0 + wn * 128 + 16 * nt + l16;
+        if (n >= N) continue;
         float x = acc[mt][nt][r];
-        if (GELU) x = gelu_erf(x);
-        if (n < N) Cout[(int64_t)m * N + n] = (__bf16)x;
+        if (splits > 1) {
+          part[((int64_t)z * M + m) * N + n] = x;
+        } else {
+          if (GELU) x = gelu_erf(x);
+          Cout[(int64_t)m * N + n] = (__bf16)x;
+        }
       }
     }
 }
 
-hipError_t launch_gemm_nt(const void* A, const void* B, void* C, int M, int N, int K, bool gelu, hipStream_t s) {
+// C = act(sum over z of part[z]) in split order, bf16 out; 4 elements per thread.
+template <bool GELU>
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const float4* __restrict__ part,
+                                                                 __bf16* __restrict__ Cout, int64_t n4, int splits) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    float4 v = part[i];
+    for (int z = 1; z < splits; ++z) {
+      const float4 w = part[(int64_t)z * n4 + i];
+      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
+    if (GELU) {
+      v.x = gelu_erf(v.x); v.y = gelu_erf(v.y); v.z = gelu_erf(v.z); v.w = gelu_erf(v.w);
+    }
+    __bf16* o = Cout + 4 * i;
+    o[0] = (__bf16)v.x; o[1] = (__bf16)v.y; o[2] = (__bf16)v.z; o[3] = (__bf16)v.w;
+  }
+}
+
+// K splits for an M x N x K product: enough workgroups to cover 256 CUs,
+// at most 8, dividing the K steps (K / 64), and whose fp32 partials fit in
+// part_bytes; 1 when the tile grid fills the chip.
+int gemm_splits(int M, int N, int K, size_t part_bytes) {
+  const int64_t tiles = (int64_t)((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  if (tiles >= 256 || N % 4 != 0) return 1;
+  const int steps = K / kBK;
+  int want = (int)((256 + tiles - 1) / tiles);
+  if (want > 8) want = 8;
+  for (int sp = want; sp > 1; --sp)
+    if (steps % sp == 0 && (size_t)sp * M * N * sizeof(float) <= part_bytes) return sp;
+  return 1;
+}
+
+hipError_t launch_gemm_nt(const void* A, const void* B, void* C, float* part, size_t part_bytes, int M, int N, int K,
+                          bool gelu, hipStream_t s) {
   if (M <= 0 || N <= 0 || K <= 0 || K % kBK != 0) return hipErrorInvalidValue;
-  const int64_t grid = (int64_t)((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  const int splits = part ? gemm_splits(M, N, K, part_bytes) : 1;
+  const int64_t tiles = (int64_t)((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  const int64_t grid = tiles * splits;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const __bf16* a = static_cast<const __bf16*>(A);
+  const __bf16* b = static_cast<const __bf16*>(B);
+  __bf16* c = static_cast<__bf16*>(C);
   if (gelu)
-    hipLaunchKernelGGL(gemm_nt_kernel<true>, dim3((unsigned)grid), dim3(kGemmThreads), 0, s,
-                       static_cast<const __bf16*>(A), static_cast<const __bf16*>(B), static_cast<__bf16*>(C), M, N, K);
+    hipLaunchKernelGGL(gemm_nt_kernel<true>, dim3((unsigned)grid), dim3(kGemmThreads), 0, s, a, b, c, part, M, N, K,
+                       splits);
   else
-    hipLaunchKernelGGL(gemm_nt_kernel<false>, dim3((unsigned)grid), dim3(kGemmThreads), 0, s,
-                       static_cast<const __bf16*>(A), static_cast<const __bf16*>(B), static_cast<__bf16*>(C), M, N, K);
+    hipLaunchKernelGGL(gemm_nt_kernel<false>, dim3((unsigned)grid), dim3(kGemmThreads), 0, s, a, b, c, part, M, N, K,
+                       splits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const int64_t n4 = (int64_t)M * N / 4;
+  const int64_t g = std::min<int64_t>((n4 + 255) / 256, 8192);
+  if (gelu)
+    hipLaunchKernelGGL(gemm_splitk_reduce_kernel<true>, dim3((unsigned)g), dim3(256), 0, s,
+                       reinterpret_cast<const float4*>(part), c, n4, splits);
+  else
+    hipLaunchKernelGGL(gemm_splitk_reduce_kernel<false>, dim3((unsigned)g), dim3(256), 0, s,
+                       reinterpret_cast<const float4*>(part), c, n4, splits);
   return hipGetLastError();
+}
+
+size_t gemm_partial_bytes(int M, int N, int K) {
+  const int splits = gemm_splits(M, N, K, SIZE_MAX);
+  return splits > 1 ? (size_t)splits * M * N * sizeof(float) : 0;
 }
 
 }  // namespace ra

@@ -550,39 +550,58 @@ ra_status ra_ring_decode(const ra_dims* dims, int32_t n_hosts, const void* q, co
   return RA_OK;
 }
 
-ra_status ra_ffn_workspace_size(int64_t block_rows, int32_t f, size_t* bytes) {
-  if (block_rows < 1 || f < 64 || f % 64 != 0)
-    return fail(RA_ERR_INVALID_ARG, "block_rows >= 1 and f a positive multiple of 64 (got %lld, %d)",
-                (long long)block_rows, f);
+// Feedforward workspace: the GELU output of one row block (bf16), then the
+// split-K partials of whichever layer needs more (fp32).
+struct FfnWs {
+  size_t h, part, total;
+};
+FfnWs ffn_ws(int64_t block_rows, int32_t h, int32_t f) {
+  FfnWs w;
+  w.h = 0;
+  w.part = align256((size_t)block_rows * f * 2);
+  const size_t p = std::max(ra::gemm_partial_bytes((int)block_rows, f, h), ra::gemm_partial_bytes((int)block_rows, h, f));
+  w.total = w.part + align256(p);
+  return w;
+}
+
+ra_status check_ffn_shape(int64_t block_rows, int32_t h, int32_t f) {
+  if (h < 64 || h % 64 != 0 || f < 64 || f % 64 != 0)
+    return fail(RA_ERR_INVALID_ARG, "h and f must be positive multiples of 64 (got %d, %d)", h, f);
+  if (block_rows < 1) return fail(RA_ERR_INVALID_ARG, "block_rows %lld < 1", (long long)block_rows);
+  if (block_rows > (1 << 24) || h > (1 << 20) || f > (1 << 20))
+    return fail(RA_ERR_UNSUPPORTED, "block_rows above 2^24 or h, f above 2^20");
+  return RA_OK;
+}
+
+ra_status ra_ffn_workspace_size(int64_t block_rows, int32_t h, int32_t f, size_t* bytes) {
+  RA_CHECK(check_ffn_shape(block_rows, h, f));
   if (!bytes) return fail(RA_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = align256((size_t)block_rows * f * 2);
+  *bytes = ffn_ws(block_rows, h, f).total;
   return RA_OK;
 }
 
 ra_status ra_block_ffn(const void* X, const void* W1, const void* W2, void* Y, int64_t rows, int32_t h, int32_t f,
                        int64_t block_rows, void* workspace, size_t workspace_bytes, void* stream) {
   if (rows < 0) return fail(RA_ERR_INVALID_ARG, "rows %lld < 0", (long long)rows);
-  if (h < 64 || h % 64 != 0 || f < 64 || f % 64 != 0)
-    return fail(RA_ERR_INVALID_ARG, "h and f must be positive multiples of 64 (got %d, %d)", h, f);
-  if (block_rows < 1) return fail(RA_ERR_INVALID_ARG, "block_rows %lld < 1", (long long)block_rows);
-  const int64_t wide = std::max(h, f);
-  if (block_rows * wide * 2 >= ((int64_t)1 << 31) || (int64_t)h * f * 2 >= ((int64_t)1 << 31))
-    return fail(RA_ERR_UNSUPPORTED, "a row block or a weight matrix reaches 2 GiB");
+  RA_CHECK(check_ffn_shape(block_rows, h, f));
   RA_CHECK(check_ptr(X, "X"));
   RA_CHECK(check_ptr(W1, "W1"));
   RA_CHECK(check_ptr(W2, "W2"));
   RA_CHECK(check_ptr(Y, "Y"));
   RA_CHECK(check_ptr(workspace, "workspace"));
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(RA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
-  const size_t need = align256((size_t)block_rows * f * 2);
-  if (workspace_bytes < need) return fail(RA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  const FfnWs w = ffn_ws(block_rows, h, f);
+  if (workspace_bytes < w.total) return fail(RA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, w.total);
   hipStream_t s = (hipStream_t)stream;
+  char* hbuf = static_cast<char*>(workspace) + w.h;
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.part);
   for (int64_t r0 = 0; r0 < rows; r0 += block_rows) {
     const int n = (int)std::min(block_rows, rows - r0);
     const char* x = static_cast<const char*>(X) + (size_t)r0 * h * 2;
     char* y = static_cast<char*>(Y) + (size_t)r0 * h * 2;
-    RA_HIP(ra::launch_gemm_nt(x, W1, workspace, n, f, h, true, s), "ffn first layer launch");
-    RA_HIP(ra::launch_gemm_nt(workspace, W2, y, n, h, f, false, s), "ffn second layer launch");
+    const size_t pb = w.total - w.part;              // split-K partials: used only when they fit
+    RA_HIP(ra::launch_gemm_nt(x, W1, hbuf, part, pb, n, f, h, true, s), "ffn first layer launch");
+    RA_HIP(ra::launch_gemm_nt(hbuf, W2, y, part, pb, n, h, f, false, s), "ffn second layer launch");
   }
   return RA_OK;
 }

@@ -97,8 +97,12 @@ hipError_t launch_permute(const void* src, void* dst, int batch, int heads, int 
 hipError_t launch_mask_tile(int delta, int rows, int cols, uint8_t* out, hipStream_t s);
 hipError_t launch_spin(uint64_t cycles, hipStream_t s);
 hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t s);
-// C [M][N] = act(A [M][K] B[N][K]^T), bf16 in and out, K % 64 == 0; act = GELU or identity
-hipError_t launch_gemm_nt(const void* A, const void* B, void* C, int M, int N, int K, bool gelu, hipStream_t s);
+// C [M][N] = act(A [M][K] B[N][K]^T), bf16 in and out, K % 64 == 0; act = GELU or identity.
+// part: fp32 scratch of part_bytes for split-K partials (split only when they fit;
+// gemm_partial_bytes(M, N, K) is what the full split needs; part may be null).
+hipError_t launch_gemm_nt(const void* A, const void* B, void* C, float* part, size_t part_bytes, int M, int N, int K,
+                          bool gelu, hipStream_t s);
+size_t gemm_partial_bytes(int M, int N, int K);
 // decode split + combine; out [batch][hq][d] in out_dtype (0 bf16, 1 fp32), lse [batch][hq]
 hipError_t launch_decode(const DecArgs& a, int head_dim, void* out, float* lse, int out_dtype, hipStream_t s);
 

@@ -315,10 +315,12 @@ def test_decode_argument_checks():
 def test_ffn_argument_checks():
     """ra_block_ffn rejects bad arguments before any HIP call."""
     n = ctypes.c_size_t(0)
-    assert ra.raw_call("ra_ffn_workspace_size", 256, 512, ctypes.byref(n)) == L.RA_OK
-    assert n.value == 256 * 512 * 2
-    assert ra.raw_call("ra_ffn_workspace_size", 256, 500, ctypes.byref(n)) == L.RA_ERR_INVALID_ARG
-    assert ra.raw_call("ra_ffn_workspace_size", 0, 512, ctypes.byref(n)) == L.RA_ERR_INVALID_ARG
+    assert ra.raw_call("ra_ffn_workspace_size", 4096, 4096, 16384, ctypes.byref(n)) == L.RA_OK
+    assert n.value == 4096 * 16384 * 2                # a full grid: no split-K partials
+    assert ra.raw_call("ra_ffn_workspace_size", 256, 128, 512, ctypes.byref(n)) == L.RA_OK
+    assert n.value >= 256 * 512 * 2 + 2 * 256 * 512 * 4   # GELU output + split-K partials
+    assert ra.raw_call("ra_ffn_workspace_size", 256, 128, 500, ctypes.byref(n)) == L.RA_ERR_INVALID_ARG
+    assert ra.raw_call("ra_ffn_workspace_size", 0, 128, 512, ctypes.byref(n)) == L.RA_ERR_INVALID_ARG
     big = 1 << 40
 
     def call(x=FAKE, w1=FAKE, w2=FAKE, y=FAKE, rows=100, h=128, f=256, br=64, w=FAKE, wb=big):
@@ -331,5 +333,7 @@ def test_ffn_argument_checks():
     assert call(x=None) == L.RA_ERR_INVALID_ARG
     assert call(w2=FAKE + 2) == L.RA_ERR_INVALID_ARG
     assert call(w=FAKE + 64) == L.RA_ERR_INVALID_ARG
-    assert call(wb=64 * 256 * 2 - 1) == L.RA_ERR_WORKSPACE
-    assert call(h=65536, f=65536) == L.RA_ERR_UNSUPPORTED
+    assert ra.raw_call("ra_ffn_workspace_size", 64, 128, 256, ctypes.byref(n)) == L.RA_OK
+    assert call(wb=n.value - 1) == L.RA_ERR_WORKSPACE
+    assert call(h=1 << 21) == L.RA_ERR_UNSUPPORTED
+    assert call(br=(1 << 24) + 1) == L.RA_ERR_UNSUPPORTED
