@@ -221,3 +221,72 @@ def test_ring_bwd_zigzag_mid_sampled(torch):
     _compare("ring_bwd zigzag mid dQ", _gather(dQ, rows), dQr)
     _compare("ring_bwd zigzag mid dK", _gather(dK, krows, heads), dKr)
     _compare("ring_bwd zigzag mid dV", _gather(dV, krows, heads), dVr)
+
+
+@pytest.mark.timeout(900)
+def test_ring_bwd_64k_closed_form_zero_keys(torch):
+    """Backward workload at full size with K = 0, every row checked.
+    All scores are 0, so each visible key gets probability 1 / (t_q + 1)
+    (causal contiguous: token t_q sees tokens 0..t_q).  The gradient of
+    softmax attention then has closed forms in token order:
+      dQ = scale dS K = 0 exactly (every product has a zero factor);
+      dV_k = sum over q >= k of dO_q / (q + 1), a reverse cumulative sum;
+      dK_k = scale sum over q >= k of (dO_q . v_k - D_q) Q_q / (q + 1),
+    with D_q = dO_q . O_q and O_q the prefix mean of V.  dV is compared on
+    every key row of every head, dK on 256 seeded key rows of 4 seeded
+    heads (the d x d suffix sums of Q_q dO_q^T are evaluated only there)."""
+    import long_context_transformers_amd as ra
+    w = rs.workloads()["bwd_64k"]
+    N, Hq, c, d = w.n_hosts, w.heads_q, w.block_len, w.head_dim
+    S = N * c
+    inp = H.inputs(w, with_do=True)
+    q, v, do = (H.dev_tensor(x, w.dtype) for x in (inp.q_dev, inp.v_dev, inp.do_dev))
+    k = torch.zeros_like(q)
+    O, lse = _fwd(torch, w, q, k, v)
+    cfg = H.cfg_of(w)
+    dQ = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    dK = torch.empty(k.shape, dtype=torch.float32, device="cuda")
+    dV = torch.empty(v.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(ra.ring_workspace_size(cfg, True), dtype=torch.uint8, device="cuda")
+    ra.ring_bwd(cfg, q, k, v, O, lse, do, dQ, dK, dV, ws, torch.cuda.current_stream(),
+                torch.cuda.Stream())
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(dQ)) == 0, "dQ must be exactly zero when K = 0"
+
+    def tok(x, h):        # host-major [N][1][H][c][d] -> token-ordered [S, d] of head h (fp64)
+        return np.ascontiguousarray(x[:, 0, h]).reshape(S, d).astype(np.float64)
+
+    inv = 1.0 / np.arange(1, S + 1, dtype=np.float64)
+    scale = 1.0 / np.sqrt(d)
+    err_v = 0.0
+    for h in range(Hq):
+        dOh = tok(inp.do_f32, h)
+        want = np.cumsum((dOh * inv[:, None])[::-1], axis=0)[::-1]
+        got = dV[:, 0, h].float().cpu().numpy().reshape(S, d)
+        err_v = max(err_v, float(np.abs(got - want).max()))
+        assert np.all(np.isfinite(got))
+    H.report("ring_bwd bwd_64k K=0 dV (all rows)", max_abs=err_v)
+    assert err_v <= TOL_BWD, err_v
+
+    rng = np.random.default_rng(9700 + w.cfg)
+    heads = sorted(rng.choice(Hq, 4, replace=False).tolist())
+    err_k = 0.0
+    for h in heads:
+        Qh, Vh, dOh = tok(inp.q_f32, h), tok(inp.v_f32, h), tok(inp.do_f32, h)
+        Oh = np.cumsum(Vh, axis=0) * inv[:, None]
+        Dq = (dOh * Oh).sum(axis=1)
+        ks = np.sort(np.unique(np.concatenate([[0, 1, S - 1], rng.choice(S, 253, replace=False)])))[::-1]
+        M = np.zeros((d, d))          # sum over q >= k of Q_q dO_q^T / (q + 1)
+        u = np.zeros(d)               # sum over q >= k of D_q Q_q / (q + 1)
+        hi = S
+        want = np.empty((len(ks), d))
+        for i, kr in enumerate(ks):
+            wq = Qh[kr:hi] * inv[kr:hi, None]
+            M += wq.T @ dOh[kr:hi]
+            u += (wq * Dq[kr:hi, None]).sum(axis=0)
+            hi = kr
+            want[i] = scale * (M @ Vh[kr] - u)
+        got = dK[:, 0, h].float().cpu().numpy().reshape(S, d)[ks]
+        err_k = max(err_k, float(np.abs(got - want).max()))
+    H.report("ring_bwd bwd_64k K=0 dK (sampled rows)", max_abs=err_k, heads=heads)
+    assert err_k <= TOL_BWD, err_k

@@ -438,6 +438,27 @@ def test_backward_numpy_closed_form_matches_c():
             assert np.allclose(dV[h, 0, 0], dv[t], atol=1e-12)
 
 
+def test_backward_zero_keys_closed_form():
+    """K = 0 under the causal contiguous mask: token t_q gives probability
+    1/(t_q + 1) to each of tokens 0..t_q, so dQ = 0, dV_k is the reverse
+    cumulative sum of dO_q/(q + 1), and dK_k = scale * sum over q >= k of
+    (dO_q . v_k - D_q) Q_q/(q + 1) with D_q = dO_q . (prefix mean of V)_q."""
+    N, c, d = 3, 5, 4
+    S = N * c
+    q = _rand(131, (N, 1, 1, c, d)); k = np.zeros((N, 1, 1, c, d), np.float32)
+    v = _rand(132, (N, 1, 1, c, d)); do = _rand(133, (N, 1, 1, c, d))
+    _, dQ, dK, dV = _loss_and_grads(q, k, v, do, C, 1, N)
+    qf, vf, dof = (npref.gather_full(x, C)[0, 0].astype(np.float64) for x in (q, v, do))
+    inv = 1.0 / np.arange(1, S + 1)
+    dv_ref = np.cumsum((dof * inv[:, None])[::-1], axis=0)[::-1]
+    D = (dof * np.cumsum(vf, axis=0) * inv[:, None]).sum(axis=1)
+    dk_ref = np.array([sum((dof[t] @ vf[j] - D[t]) * inv[t] * qf[t] for t in range(j, S))
+                       for j in range(S)]) / math.sqrt(d)
+    assert np.abs(dQ).max() == 0.0
+    assert np.allclose(dV.reshape(S, d), dv_ref, atol=1e-13, rtol=0)
+    assert np.allclose(dK.reshape(S, d), dk_ref, atol=1e-13, rtol=0)
+
+
 def test_backward_equal_value_rows_give_zero_dq_dk():
     """All V rows equal => O is that row for every query, dP - D = 0 on every
     visible pair, so dQ = dK = 0 exactly (up to rounding)."""
