@@ -217,7 +217,8 @@ def tcalc_sweep(torch, ra, reps=5):
 
 
 def elementwise_bw(torch, ra, reps=10):
-    """Finalize and merge at one 256K-host shape (32 heads, c = 32768, d = 128)."""
+    """Finalize, merge and the backward preprocess at one 256K-host shape
+    (32 heads, c = 32768, d = 128)."""
     B, Hq, c, d = 1, 32, 32768, 128
     dims = ra.Dims(B, Hq, Hq, d, c, rs.DT_BF16)
     rows = B * Hq * c
@@ -242,12 +243,17 @@ def elementwise_bw(torch, ra, reps=10):
         b.synchronize()
         return a.elapsed_time(b) / reps / 1e3
 
+    dO = torch.randn((B, Hq, c, d), device="cuda").to(torch.bfloat16)
+    Dd = torch.empty((B, Hq, c), device="cuda")
     tf = timeit(lambda: ra.finalize(dims, m, l, O, Ob, lse))
     tm = timeit(lambda: ra.merge_lse(dims, O, m, O2, l2, Om, lm))
+    tp = timeit(lambda: ra.bwd_preprocess(dims, Ob, dO, Dd))
     fin_bytes = rows * (6 * d + 12)     # O fp32 read, m, l read, bf16 out, lse out
     mer_bytes = rows * (12 * d + 12)    # two fp32 O in, one out, three lse
+    pre_bytes = rows * (4 * d + 4)      # bf16 O and dO in, D out
     return {"finalize": {"s": tf, "GBs": fin_bytes / tf / 1e9, "bytes_per_row": 6 * d + 12},
             "merge": {"s": tm, "GBs": mer_bytes / tm / 1e9, "bytes_per_row": 12 * d + 12},
+            "bwd_preprocess": {"s": tp, "GBs": pre_bytes / tp / 1e9, "bytes_per_row": 4 * d + 4},
             "peak_GBs": PEAK_HBM_GBS}
 
 
