@@ -120,17 +120,38 @@ void dkdv_kernel(BwdArgs a) {
       vf[ks][kk] = as_bf16x8(bload16(rv, (kr * D + 32 * kk + 8 * g) * 2));
     }
   // dK, dV accumulators: sub-tile ks, d tile nt; value r of lane (g, i) is
-  // key kw0 + 16ks + 4g + r, d column 16nt + i.
+  // key kw0 + 16ks + 4g + r, d column 16nt + i.  They start from the partial
+  // sum received for these keys (dK divided by the scale the epilogue
+  // applies), loaded here so its latency overlaps the first tiles' loads; with
+  // one workgroup per CU, a read of it in the epilogue would stall the CU.
+  // Keys past the block end read as 0 (buffer range check).
   f32x4 acc_dk[2][NT], acc_dv[2][NT];
+  if (a.dk_in) {
+    const int64_t ioff = host * a.dkv_in_host_stride + ((int64_t)(b * a.hkv + kvh) * c) * D;
+    const __amdgpu_buffer_rsrc_t rki = rsrc(a.dk_in + ioff, c * D * 4);
+    const __amdgpu_buffer_rsrc_t rvi = rsrc(a.dv_in + ioff, c * D * 4);
+    const float inv_scale = 1.f / a.scale;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        acc_dk[ks][nt][r] = 0.f;
-        acc_dv[ks][nt][r] = 0.f;
-      }
+        for (int r = 0; r < 4; ++r) {
+          const int off = ((kw0 + 16 * ks + 4 * g + r) * D + 16 * nt + l16) * 4;
+          acc_dk[ks][nt][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rki, off, 0, 0)) * inv_scale;
+          acc_dv[ks][nt][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rvi, off, 0, 0));
+        }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc_dk[ks][nt][r] = 0.f;
+          acc_dv[ks][nt][r] = 0.f;
+        }
+  }
 
   // Query segments with one visibility offset each: the whole block, or, for
   // a zigzag block (zz_half = c/2, a multiple of BK), the two query halves
@@ -346,9 +367,9 @@ void dkdv_kernel(BwdArgs a) {
     for (int it = itl[sg]; it < ib[sg + 1]; ++it) step(it, std::true_type{});
   }
 
-  // epilogue: out = in + contribution (scale on dK).  The accumulators are
-  // staged through the (idle) LDS stages as row-major fp32 [BK keys][D] for
-  // dK then dV, so the read of the partial sum and the store run as
+  // epilogue: out = (in + contribution) (scale on dK), the accumulators
+  // having started from `in`.  They are staged through the (idle) LDS stages
+  // as row-major fp32 [BK keys][D] for dK then dV, so the store runs as
   // contiguous 16-byte accesses.  No LDS-DMA is in flight here: the last
   // iteration waited for every issued tile.
   static_assert(2 * BK * D * 4 <= NS * BUF, "epilogue staging must fit in the LDS stages");
@@ -367,29 +388,16 @@ void dkdv_kernel(BwdArgs a) {
   __syncthreads();
   const int out_host = (host + a.dkv_out_host_shift) % a.n_hosts;
   const int64_t ooff = out_host * a.dkv_out_host_stride + ((int64_t)(b * a.hkv + kvh) * c + k0) * D;
-  const int64_t ioff = host * a.dkv_in_host_stride + ((int64_t)(b * a.hkv + kvh) * c + k0) * D;
   const int valid = min(BK, c - k0) * D;                     // floats of this workgroup's keys
   constexpr int V4 = BK * D / 4 / kBwdThreads;              // float4 per thread per matrix
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     float* out = (m == 0 ? a.dk_out : a.dv_out) + ooff;
-    const float* in = (m == 0 ? a.dk_in : a.dv_in);
     float4 v[V4];
 #pragma unroll
     for (int j = 0; j < V4; ++j) {
       const int e = 4 * (j * kBwdThreads + tid);
       v[j] = *reinterpret_cast<const float4*>(st + m * BK * D + e);
-    }
-    if (in) {
-      in += ioff;
-#pragma unroll
-      for (int j = 0; j < V4; ++j) {
-        const int e = 4 * (j * kBwdThreads + tid);
-        if (e < valid) {
-          const float4 o = *reinterpret_cast<const float4*>(in + e);
-          v[j].x += o.x; v[j].y += o.y; v[j].z += o.z; v[j].w += o.w;
-        }
-      }
     }
 #pragma unroll
     for (int j = 0; j < V4; ++j) {
