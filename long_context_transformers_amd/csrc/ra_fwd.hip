@@ -191,8 +191,17 @@ void fwd_bf16_kernel(FwdArgs a) {
   }
 
   // ---- LDS-DMA tile loads and loop-invariant LDS offsets ----
-  auto dma_k = [&](int t, int buf) { SK::dma(rk, smem + buf * TILE, t * kBN, wave, lane); };
-  auto dma_v = [&](int t, int buf) { S::dma(rv, smem + (2 + buf) * TILE, t * kBN, wave, lane); };
+  // A tile's first row goes into the buffer descriptor (scalar arithmetic;
+  // the range still ends at the block's end), so the per-lane offsets of the
+  // LDS-DMA loads are loop-invariant and a tile costs no VALU to address.
+  auto dma_k = [&](int t, int buf) {
+    const int off = t * kBN * S::ROWB;
+    SK::dma(tile::rsrc(reinterpret_cast<const char*>(kp) + off, blk_bytes - off), smem + buf * TILE, 0, wave, lane);
+  };
+  auto dma_v = [&](int t, int buf) {
+    const int off = t * kBN * S::ROWB;
+    S::dma(tile::rsrc(reinterpret_cast<const char*>(vp) + off, blk_bytes - off), smem + (2 + buf) * TILE, 0, wave, lane);
+  };
   // row reads of K: row 16mt + i, global chunk 4kk + g
   int roff[NKK];
 #pragma unroll
