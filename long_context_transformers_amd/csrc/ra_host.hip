@@ -244,8 +244,17 @@ struct RingEvents {
 // The copies run on the DMA engines (hipMemcpyDeviceToDeviceNoCU), as a
 // neighbour's send would arrive, so they take no compute units from the
 // block kernels running meanwhile (blit-kernel copies cost those kernels
-// about 2% of their speed on the non-causal 32K ring).
-constexpr hipMemcpyKind kRingCopy = hipMemcpyDeviceToDeviceNoCU;
+// about 2% of their speed on the non-causal 32K ring).  Where the runtime
+// refuses that kind (DMA engines disabled for device-local copies), the copy
+// is enqueued as an ordinary device-to-device copy instead.
+hipError_t ring_copy(void* dst, const void* src, size_t bytes, hipStream_t comm) {
+  hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDeviceNoCU, comm);
+  if (e == hipErrorInvalidValue || e == hipErrorInvalidMemcpyDirection || e == hipErrorNotSupported) {
+    (void)hipGetLastError();
+    e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, comm);
+  }
+  return e;
+}
 ra_status enqueue_transfer(const ra_ring_cfg* cfg, int s, const char* K, const char* V, char* rk, char* rv,
                            size_t blk, hipStream_t comm, ra_ring_stats* st, std::vector<int>* per_host) {
   const int N = cfg->n_hosts, hb = cfg->host_begin, na = cfg->host_end - cfg->host_begin;
@@ -257,11 +266,11 @@ ra_status enqueue_transfer(const ra_ring_cfg* cfg, int s, const char* K, const c
     const char* sk = s == 0 ? K : rk + (size_t)cur * na * blk;
     const char* sv = s == 0 ? V : rv + (size_t)cur * na * blk;
     if (N > 1) {
-      RA_HIP(hipMemcpyAsync(dk + blk, sk, (size_t)(N - 1) * blk, kRingCopy, comm), "ring copy K");
-      RA_HIP(hipMemcpyAsync(dv + blk, sv, (size_t)(N - 1) * blk, kRingCopy, comm), "ring copy V");
+      RA_HIP(ring_copy(dk + blk, sk, (size_t)(N - 1) * blk, comm), "ring copy K");
+      RA_HIP(ring_copy(dv + blk, sv, (size_t)(N - 1) * blk, comm), "ring copy V");
     }
-    RA_HIP(hipMemcpyAsync(dk, sk + (size_t)(N - 1) * blk, blk, kRingCopy, comm), "ring copy K");
-    RA_HIP(hipMemcpyAsync(dv, sv + (size_t)(N - 1) * blk, blk, kRingCopy, comm), "ring copy V");
+    RA_HIP(ring_copy(dk, sk + (size_t)(N - 1) * blk, blk, comm), "ring copy K");
+    RA_HIP(ring_copy(dv, sv + (size_t)(N - 1) * blk, blk, comm), "ring copy V");
     st->copy_bytes += (int64_t)2 * N * blk;
     for (int a = 0; a < na; ++a) (*per_host)[a]++;
     return RA_OK;
@@ -271,9 +280,9 @@ ra_status enqueue_transfer(const ra_ring_cfg* cfg, int s, const char* K, const c
     ra_step nx;
     schedule_one(N, h, cfg->dims.block_len, cfg->layout, cfg->mask, s + 1, &nx);
     if ((cfg->flags & RA_FLAG_ELIDE_SKIPPED_COPIES) && nx.cls == RA_BLK_SKIP) continue;
-    RA_HIP(hipMemcpyAsync(dk + (size_t)a * blk, K + (size_t)nx.src * blk, blk, kRingCopy, comm),
+    RA_HIP(ring_copy(dk + (size_t)a * blk, K + (size_t)nx.src * blk, blk, comm),
            "pool copy K");
-    RA_HIP(hipMemcpyAsync(dv + (size_t)a * blk, V + (size_t)nx.src * blk, blk, kRingCopy, comm),
+    RA_HIP(ring_copy(dv + (size_t)a * blk, V + (size_t)nx.src * blk, blk, comm),
            "pool copy V");
     st->copy_bytes += (int64_t)2 * blk;
     (*per_host)[a]++;
