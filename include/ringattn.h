@@ -16,7 +16,9 @@
  * denominator l, numerator O) ([P1] Ring Attention的核心洞察, Online Softmax;
  * [P2] 5.2; [P3] 分块注意力, 环状拓扑).  On one GPU the N hosts are virtual:
  * their blocks live in one HBM and the neighbour send/receive is an
- * asynchronous device-to-device copy on a second stream.
+ * asynchronous device-to-device copy on a second stream, run by the DMA
+ * engines (no compute units; an ordinary device copy where the runtime
+ * refuses that kind).
  *
  * Conventions shared by every call
  * --------------------------------
