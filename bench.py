@@ -535,6 +535,8 @@ def main():
              "fwd_kernel_avg_launch_ms": f_launch,
              "fwd_kernel_tflops": (fwd_flops / N) / (f_launch / 1e3) / 1e12,
              "gpu_event_ms_per_step": gpu_ms / args.steps}
+    # the forward block kernel on this workload against the dense bf16 peak
+    extra["fwd_kernel_frac_of_peak"] = extra["fwd_kernel_tflops"] / PEAK_BF16_TFLOPS
     if bwd:
         extra["bwd_kernel_avg_launch_ms"] = b_launch
         extra["bwd_step_tflops"] = (bwd_flops / N) / (b_launch / 1e3) / 1e12
