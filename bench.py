@@ -2,18 +2,23 @@
 """Benchmark of the Ring Attention hot path on one MI355X.
 
 One step = one pass of the ring over one batch of synthetic input: the ring
-forward (scheduler, side-stream K/V transfers, block kernels, finalize) and,
-when the library provides it, the ring backward (preprocess, block backward
-kernels, K/V and dK/dV rotation), on the non-causal 32K workload: batch 1,
-8 heads, d = 128, 8 virtual hosts of c = 4096 tokens, bf16 inputs.
+forward (scheduler, side-stream K/V transfers, block kernels, finalize) and
+the ring backward (preprocess, block backward kernels, K/V and dK/dV
+rotation), on the striped causal 256K workload with every host of the ring
+simulated: batch 1, 32 heads, d = 128, 8 virtual hosts of c = 32768 tokens in
+the striped layout (host h holds tokens h, h + 8, ...), bf16 inputs
+([P1] "Ring Attention如何让大模型突破百万token上下文", 因果掩码的负载均衡挑战).
 
 Throughput is attention TFLOP/s counting only computed work: 4 d per visible
 (query, key) pair in the forward, 10 d in the backward ([P2] "Ring Attention
 with Blockwise Transformers for Near Infinite Context" reading notes, 5.4:
-4 d c^2 per block pair).  Inputs are resident in HBM before the timed region.
+4 d c^2 per block pair).  Inputs are drawn on the device (seeded) and are
+resident in HBM before the timed region.
 
-Prints ONE JSON line.  Extra measurements (t_calc(c) sweep, causal and
-striped workloads, merge/finalize bandwidth) ride along under "extra".
+Prints ONE JSON line.  Extra measurements (the non-causal 32K ring with its
+60 %-of-peak target row, one host's share of the causal 256K and 786K
+workloads, t_calc(c) sweep, merge/finalize bandwidth, decode, feedforward)
+ride along under "extra".
 """
 from __future__ import annotations
 
@@ -146,32 +151,42 @@ def time_ring(ring, steps, warmup, bwd):
     return wall, gpu_ms, f_ms, b_ms
 
 
-def cpu_baseline(w, target_s=15.0):
-    """Time the fp64 oracle on a bounded sample of the workload's rows."""
+def cpu_baseline(w, ring, target_s=15.0):
+    """Time the fp64 oracle on a bounded sample of the workload's query rows
+    (evenly spaced rows of every host and head), on the bench's own inputs
+    (the device tensors, widened to float32 on the host).  Counted work: 4 d
+    per visible (query, key) pair of the sampled rows."""
     from oracle import cref
-    inp = rs.make_inputs(w)
     hosts = list(range(w.host_begin, w.host_end))
+    q = ring.q.float().cpu().numpy()
+    k = ring.k.float().cpu().numpy()
+    v = ring.v.float().cpu().numpy()
+
+    def visible_keys(h, r):
+        if w.mask == rs.MASK_NONE:
+            return w.n_hosts * w.block_len
+        return cref.token_index(w.layout, w.n_hosts, w.block_len, h, int(r)) + 1
 
     def run(n_rows):
         rows = np.arange(n_rows) * (w.block_len // n_rows)
         desc = cref.row_desc(hosts, range(w.batch), range(w.heads_q), rows)
         t0 = time.perf_counter()
-        cref.attn_rows(inp.q_f32, inp.k_f32, inp.v_f32, n_hosts=w.n_hosts, layout=w.layout,
-                       causal=w.mask, rows=desc, q_host_base=inp.q_host_base)
+        cref.attn_rows(q, k, v, n_hosts=w.n_hosts, layout=w.layout, causal=w.mask, rows=desc,
+                       q_host_base=w.host_begin)
         dt = time.perf_counter() - t0
-        pairs = len(desc) * w.n_hosts * w.block_len   # non-causal: every key visible
+        pairs = w.batch * w.heads_q * sum(visible_keys(h, r) for h in hosts for r in rows)
         return dt, pairs, len(desc)
 
-    dt, pairs, n = run(16)
-    n_rows = int(max(16, min(w.block_len, 16 * target_s / max(dt, 1e-3))))
-    n_rows = 16 * max(1, n_rows // 16)
-    if n_rows > 16:
+    dt, pairs, n = run(4)
+    n_rows = int(max(4, min(w.block_len, 4 * target_s / max(dt, 1e-3))))
+    n_rows = 4 * max(1, n_rows // 4)
+    if n_rows > 4:
         dt, pairs, n = run(n_rows)
     flops = 4.0 * w.head_dim * pairs
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cref.num_threads(),
             "kind": "oracle",
             "sample": f"{n} query rows ({n_rows} evenly spaced rows x {w.heads_q} heads x "
-                      f"{len(hosts)} hosts) of {w.name}, fp64, {dt:.1f} s wall"}
+                      f"{len(hosts)} hosts) of {w.name}, forward only, fp64, {dt:.1f} s wall"}
 
 
 def tcalc_sweep(torch, ra, reps=5):
@@ -300,9 +315,14 @@ def causal_rates(torch, ra, steps=3):
     return out
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "ring_bwd_step_noncausal_32k_hbm_traffic.md")
 BWD_SOURCES = [os.path.join(ROOT, "long_context_transformers_amd", "csrc", n)
                for n in ("ra_bwd.hip", "ra_tile.h")]   # the backward kernels' code
+
+
+def traffic_profile(w):
+    """Committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of the backward
+    step of workload w."""
+    return os.path.join(ROOT, "profiles", f"ring_bwd_step_{w.name}_hbm_traffic.md")
 
 
 def bwd_sources_sha256():
@@ -314,13 +334,13 @@ def bwd_sources_sha256():
     return h.hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(w):
     """HBM bytes per backward ring step (dK/dV + dQ kernels) from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when the kernel sources
     have changed since the counters were taken (or no summary exists)."""
     import re
     try:
-        text = open(TRAFFIC_PROFILE).read()
+        text = open(traffic_profile(w)).read()
     except OSError:
         return None
     vals = dict(re.findall(r"^- (\w+): `([^`]+)`", text, re.M))
@@ -330,11 +350,12 @@ def measured_traffic():
 
 
 def bwd_algorithmic_bytes(w):
-    """Bytes one backward ring step moves for all hosts, averaged over a ring
-    pass: the dK/dV kernel reads Q, dO, K, V (bf16), lse, D (fp32) and the
-    received dK/dV partial sums (fp32; none at the first step) and writes the
-    new sums; the dQ kernel reads Q, dO, K, V, lse, D and the fp32 dQ sum (none
-    at the first step) and writes it.  Non-causal: every block is whole."""
+    """Compulsory bytes of one backward ring step for all hosts, averaged over
+    a ring pass: the dK/dV kernel reads Q, dO, K, V (bf16), lse, D (fp32) and
+    the received dK/dV partial sums (fp32; none at the first step) and writes
+    the new sums; the dQ kernel reads Q, dO, K, V, lse, D and the fp32 dQ sum
+    (none at the first step) and writes it.  Every block pair of the
+    non-causal and striped rings touches every row, so each is read once."""
     N, c, d = w.n_hosts, w.block_len, w.head_dim
     hq, hkv = w.batch * w.heads_q, w.batch * w.heads_kv
     qo = 2 * hq * c * d * 2 + 2 * hq * c * 4         # Q, dO, lse, D
@@ -455,15 +476,74 @@ def ffn_rates(torch, ra, reps=10):
     return out
 
 
+def headline_workload():
+    """Striped causal 256K over all 8 hosts: 32 heads, d = 128, c = 32768,
+    bf16 -- the causal 256K workload with every host of the ring simulated."""
+    base = rs.workloads()["causal_256k_striped"]
+    return base.replace(name="causal_256k_striped_H32_N8_c32768_all_hosts", host_begin=0,
+                        host_end=base.n_hosts)
+
+
+def step_rates(w, f_ms, b_ms, steps):
+    """Per-launch kernel rates from the step events: forward (one launch per
+    ring step, all hosts) and backward (dK/dV + dQ launches of one ring step)."""
+    N = w.n_hosts
+    out = {"fwd_kernel_avg_launch_ms": statistics.mean(f_ms),
+           "fwd_kernel_tflops": counted_flops(w, 4) / N / (statistics.mean(f_ms) / 1e3) / 1e12,
+           "fwd_ms_per_pass": sum(f_ms) / steps}
+    if b_ms:
+        out.update({"bwd_step_avg_launch_ms": statistics.mean(b_ms),
+                    "bwd_step_tflops": counted_flops(w, 10) / N / (statistics.mean(b_ms) / 1e3) / 1e12,
+                    "bwd_ms_per_pass": sum(b_ms) / steps})
+    out["fwd_kernel_frac_of_peak"] = out["fwd_kernel_tflops"] / PEAK_BF16_TFLOPS
+    if b_ms:
+        out["bwd_step_frac_of_peak"] = out["bwd_step_tflops"] / PEAK_BF16_TFLOPS
+    return out
+
+
+def first_pass(ring):
+    """Event-timed first ring forward and backward on fresh buffers (the
+    cold pass: first touch of the workspace and output pages)."""
+    torch = ring.torch
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record()
+    st_f = ring.fwd()
+    e[1].record()
+    st_b = ring.bwd() if ring.with_bwd else None
+    e[2].record()
+    torch.cuda.synchronize()
+    return {"fwd_ms": e[0].elapsed_time(e[1]), "bwd_ms": e[1].elapsed_time(e[2]) if st_b else None}, st_f, st_b
+
+
+def noncausal_32k(torch, ra, steps, warmup):
+    """The non-causal 32K ring (8 hosts x 4096, 8 heads): whole-step rate,
+    the forward kernel and backward step against the bf16 peak (the 60 %
+    target row) -- same timing as the headline."""
+    w = rs.workloads()["noncausal_32k"]
+    ring = Ring(w, torch, ra, seed=w.cfg, with_bwd=True)
+    ring.fwd()
+    ring.bwd()
+    torch.cuda.synchronize()
+    wall, gpu_ms, f_ms, b_ms = time_ring(ring, steps, warmup, True)
+    out = {"workload": w.name + " ring fwd+bwd",
+           "tflops": counted_flops(w, 14) / (wall / steps) / 1e12, "ms_per_step": wall * 1e3 / steps}
+    out.update(step_rates(w, f_ms, b_ms, steps))
+    out["target_frac"] = 0.60
+    del ring
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--no-bwd", action="store_true", help="time the ring forward only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--workload", choices=["headline", "noncausal_32k"], default="headline",
+                    help="what the timed steps run (profiling runs may pick the non-causal 32K ring)")
     ap.add_argument("--ffn-only", action="store_true",
                     help="only measure the blockwise feedforward and print its JSON")
     ap.add_argument("--decode-only", action="store_true",
@@ -491,36 +571,29 @@ def main():
         print(json.dumps(ffn_rates(torch, ra)), flush=True)
         return
 
-    w = rs.workloads()["noncausal_32k"]
-    log(f"[bench] workload {w.name}: drawing inputs")
-    inp = rs.make_inputs(w)
-    bwd = not args.no_bwd
-    ring = Ring(w, torch, ra, inp=inp, with_bwd=True)
-    if bwd:
-        try:
-            ring.fwd()
-            ring.bwd()
-            torch.cuda.synchronize()
-        except ra.RingAttnError as e:
-            log(f"[bench] ring backward unavailable ({e}); timing the forward only")
-            bwd = False
-    log(f"[bench] timing {args.steps} steps after {args.warmup} warm-up steps (backward: {bwd})")
-    wall, gpu_ms, f_ms, b_ms = time_ring(ring, args.steps, args.warmup, bwd)
+    w = headline_workload() if args.workload == "headline" else rs.workloads()["noncausal_32k"]
+    log(f"[bench] workload {w.name}: drawing inputs on the device")
+    ring = Ring(w, torch, ra, seed=w.cfg, with_bwd=True)
+    cold, st_f, st_b = first_pass(ring)     # also checks that forward and backward run
+    log(f"[bench] first pass: forward {cold['fwd_ms']:.1f} ms, backward {cold['bwd_ms']:.1f} ms")
+    log(f"[bench] timing {args.steps} steps (ring forward + backward) after {args.warmup} warm-up steps")
+    wall, gpu_ms, f_ms, b_ms = time_ring(ring, args.steps, args.warmup, True)
     ms_per_step = wall * 1e3 / args.steps
-    fwd_flops = counted_flops(w, 4)
-    bwd_flops = counted_flops(w, 10) if bwd else 0
-    value = (fwd_flops + bwd_flops) / (ms_per_step / 1e3) / 1e12
-
-    # dominant kernel: the block kernel with the most total time per step
     N = w.n_hosts
-    f_launch = statistics.mean(f_ms)
-    b_launch = statistics.mean(b_ms) if bwd else 0.0
-    if b_launch * 1 > f_launch:
+    fwd_flops = counted_flops(w, 4)
+    bwd_flops = counted_flops(w, 10)
+    value = (fwd_flops + bwd_flops) / (ms_per_step / 1e3) / 1e12
+    rates = step_rates(w, f_ms, b_ms, args.steps)
+
+    # dominant kernel: the block kernels with the most time per step -- the
+    # backward (dK/dV + dQ launches of one ring step, all hosts)
+    f_launch, b_launch = statistics.mean(f_ms), statistics.mean(b_ms)
+    if b_launch >= f_launch:
         dom = {"kernel": "block backward (dK/dV + dQ kernels of one ring step, all hosts)",
                "flops_per_launch": bwd_flops / N, "avg_launch_ms": b_launch,
-               "traffic": measured_traffic(), "algorithmic_bytes_per_launch": bwd_algorithmic_bytes(w)}
+               "traffic": measured_traffic(w), "algorithmic_bytes_per_launch": bwd_algorithmic_bytes(w)}
     else:
-        dom = {"kernel": "fwd_bf16_kernel (one ring step, all 8 hosts)",
+        dom = {"kernel": "fwd_bf16_kernel (one ring step, all hosts)",
                "flops_per_launch": fwd_flops / N, "avg_launch_ms": f_launch, "traffic": None,
                "algorithmic_bytes_per_launch": None}
     achieved = dom["flops_per_launch"] / (dom["avg_launch_ms"] / 1e3) / 1e12
@@ -529,23 +602,34 @@ def main():
                 "kernel": dom["kernel"], "avg_launch_ms": dom["avg_launch_ms"],
                 "algorithmic_flops_per_launch": dom["flops_per_launch"],
                 "algorithmic_bytes_per_launch": dom["algorithmic_bytes_per_launch"],
-                "traffic_source": os.path.relpath(TRAFFIC_PROFILE, ROOT)}
+                "traffic_source": os.path.relpath(traffic_profile(w), ROOT)}
 
-    extra = {"fwd_tflops": fwd_flops / (sum(f_ms) / args.steps / 1e3) / 1e12,
-             "fwd_kernel_avg_launch_ms": f_launch,
-             "fwd_kernel_tflops": (fwd_flops / N) / (f_launch / 1e3) / 1e12,
-             "gpu_event_ms_per_step": gpu_ms / args.steps}
-    # the forward block kernel on this workload against the dense bf16 peak
-    extra["fwd_kernel_frac_of_peak"] = extra["fwd_kernel_tflops"] / PEAK_BF16_TFLOPS
-    if bwd:
-        extra["bwd_kernel_avg_launch_ms"] = b_launch
-        extra["bwd_step_tflops"] = (bwd_flops / N) / (b_launch / 1e3) / 1e12
+    extra = dict(rates)
+    extra["gpu_event_ms_per_step"] = gpu_ms / args.steps
+    extra["first_pass"] = cold
+    extra["copy_kind"] = {0: "none", 1: "dma_engines", 2: "fallback_device_copy"}[st_f["copy_kind"]]
+    extra["copy_kind_bwd"] = {0: "none", 1: "dma_engines", 2: "fallback_device_copy"}[st_b["copy_kind"]]
+    extra["resident_bytes_per_host"] = {"fwd": st_f["resident_bytes_per_host"],
+                                        "bwd": st_b["resident_bytes_per_host"]}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (fp64 oracle)")
+        cpu = cpu_baseline(w, ring, args.cpu_seconds)
+    del ring
+    torch.cuda.empty_cache()
     if not args.no_extra:
-        log("[bench] causal / striped workloads")
+        if w.name.startswith("noncausal_32k"):
+            extra["noncausal_32k"] = dict(rates, workload=w.name, target_frac=0.60)
+        else:
+            log("[bench] non-causal 32K ring (60 % target row)")
+            extra["noncausal_32k"] = noncausal_32k(torch, ra, max(3, args.steps), 2)
+            nc = extra["noncausal_32k"]
+            # like for like: per-launch kernel rates of whole ring steps over all hosts
+            extra["striped_vs_noncausal_per_flop"] = {
+                "fwd": rates["fwd_kernel_tflops"] / nc["fwd_kernel_tflops"],
+                "bwd": rates["bwd_step_tflops"] / nc["bwd_step_tflops"]}
+        log("[bench] one host's share: causal 256K (contiguous, striped, zigzag) and 786K striped GQA forward")
         extra["causal"] = causal_rates(torch, ra)
-        nc_rate = extra["fwd_kernel_tflops"]
-        st = extra["causal"]["causal_256k_striped"]["tflops"]
-        extra["striped_vs_noncausal_per_flop"] = st / nc_rate
         log("[bench] causal 64K forward + backward")
         extra["causal_bwd"] = bwd_rates(torch, ra)
         log("[bench] decode against a ring-sharded KV cache")
@@ -559,21 +643,17 @@ def main():
         log("[bench] reference bf16 GEMM")
         extra["reference_gemm"] = reference_gemm(torch)
         extra["dominant_kernel_vs_reference_gemm"] = achieved / extra["reference_gemm"]["tflops"]
-        extra["fwd_kernel_vs_reference_gemm"] = extra["fwd_kernel_tflops"] / extra["reference_gemm"]["tflops"]
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (fp64 oracle)")
-        cpu = cpu_baseline(w, args.cpu_seconds)
 
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name + (" ring fwd+bwd" if bwd else " ring fwd"), "global_batch": w.batch,
+        "config": {"workload": w.name + " ring fwd+bwd", "global_batch": w.batch,
                    "seq_len": w.seq_len, "heads": w.heads_q, "head_dim": w.head_dim,
                    "virtual_hosts": w.n_hosts, "block_len": w.block_len,
-                   "parallelism": "ring of 8 virtual hosts on 1 GPU"},
+                   "layout": {0: "contiguous", 1: "striped", 2: "zigzag"}[w.layout],
+                   "mask": "causal" if w.mask else "none",
+                   "parallelism": f"ring of {w.n_hosts} virtual hosts on 1 GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extra": extra,

@@ -148,7 +148,14 @@ typedef struct {
     int32_t kernel_launches;
     int64_t copy_bytes;       /* bytes moved by the side-stream copies */
     int64_t resident_bytes_per_host; /* ring buffers one virtual host holds, see ra_ring_workspace_size */
+    int32_t copy_kind;        /* ra_copy_kind of the side-stream copies enqueued */
+    int32_t pad_;
 } ra_ring_stats;
+
+/* How the ring transfers ran: on the DMA engines (no compute units, as a
+ * neighbour's send arrives), or as an ordinary device copy because the
+ * runtime refused the DMA-engine kind for at least one copy of the call. */
+typedef enum { RA_COPY_NONE = 0, RA_COPY_DMA_ENGINES = 1, RA_COPY_FALLBACK = 2 } ra_copy_kind;
 
 /* ---------------------------------------------------------------------
  * Scheduler (host code, no device work)
@@ -287,6 +294,10 @@ ra_status ra_ring_fwd(const ra_ring_cfg *cfg, const void *Q, const void *K, cons
 /* Ring backward for all N hosts (host_begin = 0, host_end = N):
  *   Q, O, dO: [N][B][Hq][c][d] (dims->dtype); lse: [N][B][Hq][c] fp32 from
  *   ra_ring_fwd; K, V: [N][B][Hkv][c][d].
+ * bf16 inputs run on the MFMA kernels; fp32 inputs (small problems) on plain
+ * fp32 kernels.  Causal zigzag needs bf16 and block_len % 256 == 0.  Every
+ * refusal (RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_WORKSPACE) happens
+ * before the first HIP call, so a refused call enqueues nothing.
  *   dQ: [N][B][Hq][c][d] fp32 out; dK, dV: [N][B][Hkv][c][d] fp32 out.
  * K/V rotate as in the forward (side-stream copies); the fp32 dK/dV
  * accumulators travel with their block: the step kernel adds its

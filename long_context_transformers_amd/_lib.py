@@ -19,6 +19,7 @@ RA_LAYOUT_CONTIGUOUS, RA_LAYOUT_STRIPED, RA_LAYOUT_ZIGZAG = 0, 1, 2
 RA_BLK_SKIP, RA_BLK_FULL, RA_BLK_TRI_INCL, RA_BLK_TRI_STRICT, RA_BLK_BAND, RA_BLK_QUADRANTS = range(6)
 RA_FLAG_ELIDE_SKIPPED_COPIES = 1
 RA_FLAG_SERIALIZE = 2
+RA_COPY_NONE, RA_COPY_DMA_ENGINES, RA_COPY_FALLBACK = 0, 1, 2
 
 c_i32, c_i64, c_u32, c_f32, c_vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
                                     ctypes.c_float, ctypes.c_void_p)
@@ -45,7 +46,8 @@ class RaRingCfg(ctypes.Structure):
 class RaRingStats(ctypes.Structure):
     _fields_ = [("compute_steps", c_i32), ("transfers", c_i32),
                 ("skipped_blocks", c_i32), ("kernel_launches", c_i32),
-                ("copy_bytes", c_i64), ("resident_bytes_per_host", c_i64)]
+                ("copy_bytes", c_i64), ("resident_bytes_per_host", c_i64),
+                ("copy_kind", c_i32), ("pad_", c_i32)]
 
 
 P = ctypes.POINTER

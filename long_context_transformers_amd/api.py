@@ -16,7 +16,8 @@ c_vp_t = ctypes.c_void_p
 from ._lib import (RA_BF16, RA_F32, RA_MASK_NONE, RA_MASK_CAUSAL, RA_LAYOUT_CONTIGUOUS,
                    RA_LAYOUT_STRIPED, RA_LAYOUT_ZIGZAG, RA_BLK_SKIP, RA_BLK_FULL, RA_BLK_TRI_INCL,
                    RA_BLK_TRI_STRICT, RA_BLK_BAND, RA_BLK_QUADRANTS, RA_FLAG_ELIDE_SKIPPED_COPIES,
-                   RA_FLAG_SERIALIZE, RingAttnError)
+                   RA_FLAG_SERIALIZE, RA_COPY_NONE, RA_COPY_DMA_ENGINES, RA_COPY_FALLBACK,
+                   RingAttnError)
 
 
 @dataclasses.dataclass

@@ -647,6 +647,198 @@ void dq_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp32 variant (small problems, e.g. the tiny fp32 check): the same closed
+// form in plain fp32 FMAs, no MFMA.  Four lanes share one row (key row for
+// dK/dV, query row for dQ), each holding a quarter of its d columns; dot
+// products are summed over the four lanes with two exchanges.  The other
+// side's rows stream through LDS in tiles of 64.  Same argument conventions
+// as the bf16 kernels (host striding, received partial sums, neighbour
+// output, dQ accumulate flag); no zigzag quadrants.
+// ---------------------------------------------------------------------------
+constexpr int kF32Rows = 64;   // rows per workgroup and per LDS tile
+
+__device__ inline float quad_sum(float x) {
+  x += __shfl_xor(x, 1);
+  return x + __shfl_xor(x, 2);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_f32_kernel(BwdArgs a) {
+  constexpr int DQ = D / 4;                                 // columns per lane
+  __shared__ float qs[kF32Rows * D], os[kF32Rows * D], ls[kF32Rows], dsv[kF32Rows];
+  const int c = a.c;
+  const int n_kt = (c + kF32Rows - 1) / kF32Rows;
+  int L = blockIdx.x;
+  const int kt = L % n_kt;
+  L /= n_kt;
+  const int host = L % a.n_hosts;
+  L /= a.n_hosts;
+  const int kvh = L % a.hkv;
+  const int b = L / a.hkv;
+  const int group = a.hq / a.hkv;
+  const int tid = threadIdx.x, qd = tid & 3;
+  const int kr = kt * kF32Rows + (tid >> 2);
+  const bool key_ok = kr < c;
+  const int col0 = qd * DQ;
+  const int delta = a.delta[host];
+
+  const int64_t kvoff = host * a.kv_host_stride + ((int64_t)(b * a.hkv + kvh) * c) * D;
+  const float* kp = reinterpret_cast<const float*>(a.k) + kvoff;
+  const float* vp = reinterpret_cast<const float*>(a.v) + kvoff;
+  float kf[DQ], vf[DQ], dk[DQ], dv[DQ];
+  const int64_t ioff = host * a.dkv_in_host_stride + ((int64_t)(b * a.hkv + kvh) * c) * D;
+#pragma unroll
+  for (int j = 0; j < DQ; ++j) {
+    const int64_t e = (int64_t)kr * D + col0 + j;
+    kf[j] = key_ok ? kp[e] : 0.f;
+    vf[j] = key_ok ? vp[e] : 0.f;
+    dk[j] = (key_ok && a.dk_in) ? a.dk_in[ioff + e] / a.scale : 0.f;
+    dv[j] = (key_ok && a.dv_in) ? a.dv_in[ioff + e] : 0.f;
+  }
+  const float c2 = a.scale_log2;
+  const int n_qt = (c + kF32Rows - 1) / kF32Rows;
+  for (int hg = 0; hg < group; ++hg) {
+    const int head = kvh * group + hg;
+    const int64_t qoff = host * a.q_host_stride + ((int64_t)(b * a.hq + head) * c) * D;
+    const float* qp = reinterpret_cast<const float*>(a.q) + qoff;
+    const float* op = reinterpret_cast<const float*>(a.dO) + qoff;
+    const int64_t so = host * a.ml_host_stride + (int64_t)(b * a.hq + head) * c;
+    for (int t = 0; t < n_qt; ++t) {
+      const int q0 = t * kF32Rows;
+      __syncthreads();
+      for (int i = tid; i < kF32Rows * D; i += 256) {
+        const int r = q0 + i / D;
+        qs[i] = r < c ? qp[(int64_t)q0 * D + i] : 0.f;
+        os[i] = r < c ? op[(int64_t)q0 * D + i] : 0.f;
+      }
+      if (tid < kF32Rows) {
+        const int r = q0 + tid;
+        const float lv = r < c ? a.lse[so + r] : -INFINITY;
+        ls[tid] = lv * kBwdLog2e;
+        dsv[tid] = r < c ? a.D[so + r] : 0.f;
+      }
+      __syncthreads();
+      for (int i = 0; i < kF32Rows; ++i) {
+        const int qr = q0 + i;
+        float s = 0.f, dp = 0.f;
+#pragma unroll
+        for (int j = 0; j < DQ; ++j) {
+          s = __builtin_fmaf(qs[i * D + col0 + j], kf[j], s);
+          dp = __builtin_fmaf(os[i * D + col0 + j], vf[j], dp);
+        }
+        s = quad_sum(s);
+        dp = quad_sum(dp);
+        const bool vis = key_ok && qr < c && visible(kr - qr, delta) && ls[i] != -INFINITY;
+        const float p = vis ? exp2f(__builtin_fmaf(s, c2, -ls[i])) : 0.f;
+        const float ds = p * (dp - dsv[i]);
+#pragma unroll
+        for (int j = 0; j < DQ; ++j) {
+          dv[j] = __builtin_fmaf(p, os[i * D + col0 + j], dv[j]);
+          dk[j] = __builtin_fmaf(ds, qs[i * D + col0 + j], dk[j]);
+        }
+      }
+    }
+  }
+  if (!key_ok) return;
+  const int out_host = (host + a.dkv_out_host_shift) % a.n_hosts;
+  const int64_t ooff = out_host * a.dkv_out_host_stride + ((int64_t)(b * a.hkv + kvh) * c) * D;
+#pragma unroll
+  for (int j = 0; j < DQ; ++j) {
+    const int64_t e = (int64_t)kr * D + col0 + j;
+    a.dk_out[ooff + e] = a.scale * dk[j];
+    a.dv_out[ooff + e] = dv[j];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void dq_f32_kernel(BwdArgs a) {
+  constexpr int DQ = D / 4;
+  __shared__ float ks[kF32Rows * D], vs[kF32Rows * D];
+  const int c = a.c;
+  const int n_rt = (c + kF32Rows - 1) / kF32Rows;
+  int L = blockIdx.x;
+  const int rt = L % n_rt;
+  L /= n_rt;
+  const int host = L % a.n_hosts;
+  L /= a.n_hosts;
+  const int head = L % a.hq;
+  const int b = L / a.hq;
+  const int kvh = head / (a.hq / a.hkv);
+  const int tid = threadIdx.x, qd = tid & 3;
+  const int qr = rt * kF32Rows + (tid >> 2);
+  const bool row_ok = qr < c;
+  const int col0 = qd * DQ;
+  const int delta = a.delta[host];
+
+  const int64_t qoff = host * a.q_host_stride + ((int64_t)(b * a.hq + head) * c) * D;
+  const float* qp = reinterpret_cast<const float*>(a.q) + qoff;
+  const float* op = reinterpret_cast<const float*>(a.dO) + qoff;
+  const int64_t kvoff = host * a.kv_host_stride + ((int64_t)(b * a.hkv + kvh) * c) * D;
+  const float* kp = reinterpret_cast<const float*>(a.k) + kvoff;
+  const float* vp = reinterpret_cast<const float*>(a.v) + kvoff;
+  const int64_t so = host * a.ml_host_stride + (int64_t)(b * a.hq + head) * c;
+  float qf[DQ], of[DQ], dq[DQ];
+#pragma unroll
+  for (int j = 0; j < DQ; ++j) {
+    const int64_t e = (int64_t)qr * D + col0 + j;
+    qf[j] = row_ok ? qp[e] : 0.f;
+    of[j] = row_ok ? op[e] : 0.f;
+    dq[j] = 0.f;
+  }
+  const float lse2 = row_ok ? a.lse[so + qr] * kBwdLog2e : -INFINITY;
+  const float Dq = row_ok ? a.D[so + qr] : 0.f;
+  const float c2 = a.scale_log2;
+  const int n_kt = (c + kF32Rows - 1) / kF32Rows;
+  for (int t = 0; t < n_kt; ++t) {
+    const int k0 = t * kF32Rows;
+    __syncthreads();
+    for (int i = tid; i < kF32Rows * D; i += 256) {
+      const int r = k0 + i / D;
+      ks[i] = r < c ? kp[(int64_t)k0 * D + i] : 0.f;
+      vs[i] = r < c ? vp[(int64_t)k0 * D + i] : 0.f;
+    }
+    __syncthreads();
+    for (int i = 0; i < kF32Rows; ++i) {
+      const int kr = k0 + i;
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int j = 0; j < DQ; ++j) {
+        s = __builtin_fmaf(qf[j], ks[i * D + col0 + j], s);
+        dp = __builtin_fmaf(of[j], vs[i * D + col0 + j], dp);
+      }
+      s = quad_sum(s);
+      dp = quad_sum(dp);
+      const bool vis = row_ok && kr < c && visible(kr - qr, delta) && lse2 != -INFINITY;
+      const float p = vis ? exp2f(__builtin_fmaf(s, c2, -lse2)) : 0.f;
+      const float ds = p * (dp - Dq);
+#pragma unroll
+      for (int j = 0; j < DQ; ++j) dq[j] = __builtin_fmaf(ds, ks[i * D + col0 + j], dq[j]);
+    }
+  }
+  if (!row_ok) return;
+  float* dqp = a.dq + qoff;
+#pragma unroll
+  for (int j = 0; j < DQ; ++j) {
+    const int64_t e = (int64_t)qr * D + col0 + j;
+    const float v = a.scale * dq[j];
+    dqp[e] = a.dq_accumulate ? dqp[e] + v : v;
+  }
+}
+
+template <int D>
+static hipError_t launch_bwd_f32_t(const BwdArgs& a, hipStream_t s) {
+  const int64_t n_t = (a.c + kF32Rows - 1) / kF32Rows;
+  const int64_t g1 = n_t * a.hkv * a.batch * a.n_hosts;
+  const int64_t g2 = n_t * a.hq * a.batch * a.n_hosts;
+  if (g1 > 0x7fffffff || g2 > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(dkdv_f32_kernel<D>, dim3((unsigned)g1), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dq_f32_kernel<D>, dim3((unsigned)g2), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int D, int HPW>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   const int n_kt = (a.c + 127) / 128;
@@ -663,7 +855,13 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int head_dim, int dtype, hipStream_t s) {
-  if (dtype != 0) return hipErrorNotSupported;   // backward kernels: bf16 inputs
+  if (dtype == 1) {                               // fp32 inputs: no zigzag quadrants
+    if (a.zz_half != 0) return hipErrorNotSupported;
+    if (head_dim == 128) return launch_bwd_f32_t<128>(a, s);
+    if (head_dim == 64) return launch_bwd_f32_t<64>(a, s);
+    return hipErrorNotSupported;
+  }
+  if (dtype != 0) return hipErrorNotSupported;
   const int group = a.hq / a.hkv;
   const int hpw = (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
   if (head_dim == 128) {

@@ -247,11 +247,16 @@ struct RingEvents {
 // about 2% of their speed on the non-causal 32K ring).  Where the runtime
 // refuses that kind (DMA engines disabled for device-local copies), the copy
 // is enqueued as an ordinary device-to-device copy instead.
-hipError_t ring_copy(void* dst, const void* src, size_t bytes, hipStream_t comm) {
+// The kind that ran is recorded in st->copy_kind (RA_COPY_DMA_ENGINES, or
+// RA_COPY_FALLBACK once any copy of the call fell back).
+hipError_t ring_copy(void* dst, const void* src, size_t bytes, hipStream_t comm, ra_ring_stats* st) {
   hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDeviceNoCU, comm);
   if (e == hipErrorInvalidValue || e == hipErrorInvalidMemcpyDirection || e == hipErrorNotSupported) {
     (void)hipGetLastError();
     e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, comm);
+    if (e == hipSuccess) st->copy_kind = RA_COPY_FALLBACK;
+  } else if (e == hipSuccess && st->copy_kind == RA_COPY_NONE) {
+    st->copy_kind = RA_COPY_DMA_ENGINES;
   }
   return e;
 }
@@ -266,11 +271,11 @@ ra_status enqueue_transfer(const ra_ring_cfg* cfg, int s, const char* K, const c
     const char* sk = s == 0 ? K : rk + (size_t)cur * na * blk;
     const char* sv = s == 0 ? V : rv + (size_t)cur * na * blk;
     if (N > 1) {
-      RA_HIP(ring_copy(dk + blk, sk, (size_t)(N - 1) * blk, comm), "ring copy K");
-      RA_HIP(ring_copy(dv + blk, sv, (size_t)(N - 1) * blk, comm), "ring copy V");
+      RA_HIP(ring_copy(dk + blk, sk, (size_t)(N - 1) * blk, comm, st), "ring copy K");
+      RA_HIP(ring_copy(dv + blk, sv, (size_t)(N - 1) * blk, comm, st), "ring copy V");
     }
-    RA_HIP(ring_copy(dk, sk + (size_t)(N - 1) * blk, blk, comm), "ring copy K");
-    RA_HIP(ring_copy(dv, sv + (size_t)(N - 1) * blk, blk, comm), "ring copy V");
+    RA_HIP(ring_copy(dk, sk + (size_t)(N - 1) * blk, blk, comm, st), "ring copy K");
+    RA_HIP(ring_copy(dv, sv + (size_t)(N - 1) * blk, blk, comm, st), "ring copy V");
     st->copy_bytes += (int64_t)2 * N * blk;
     for (int a = 0; a < na; ++a) (*per_host)[a]++;
     return RA_OK;
@@ -280,9 +285,9 @@ ra_status enqueue_transfer(const ra_ring_cfg* cfg, int s, const char* K, const c
     ra_step nx;
     schedule_one(N, h, cfg->dims.block_len, cfg->layout, cfg->mask, s + 1, &nx);
     if ((cfg->flags & RA_FLAG_ELIDE_SKIPPED_COPIES) && nx.cls == RA_BLK_SKIP) continue;
-    RA_HIP(ring_copy(dk + (size_t)a * blk, K + (size_t)nx.src * blk, blk, comm),
+    RA_HIP(ring_copy(dk + (size_t)a * blk, K + (size_t)nx.src * blk, blk, comm, st),
            "pool copy K");
-    RA_HIP(ring_copy(dv + (size_t)a * blk, V + (size_t)nx.src * blk, blk, comm),
+    RA_HIP(ring_copy(dv + (size_t)a * blk, V + (size_t)nx.src * blk, blk, comm, st),
            "pool copy V");
     st->copy_bytes += (int64_t)2 * blk;
     (*per_host)[a]++;
@@ -738,8 +743,8 @@ ra_status ra_ring_bwd(const ra_ring_cfg* cfg, const void* Q, const void* K, cons
   if (cfg->host_begin != 0 || cfg->host_end != cfg->n_hosts)
     return fail(RA_ERR_UNSUPPORTED, "ring backward runs every host (host_begin = 0, host_end = n_hosts)");
   const bool zz = cfg->layout == RA_LAYOUT_ZIGZAG && cfg->mask == RA_MASK_CAUSAL;
-  if (zz && cfg->dims.block_len % 256 != 0)
-    return fail(RA_ERR_UNSUPPORTED, "causal zigzag ring backward needs block_len %% 256 == 0 (got %d)",
+  if (zz && (cfg->dims.dtype != RA_BF16 || cfg->dims.block_len % 256 != 0))
+    return fail(RA_ERR_UNSUPPORTED, "causal zigzag ring backward needs bf16 and block_len %% 256 == 0 (got %d)",
                 cfg->dims.block_len);
   if (cfg->flags & RA_FLAG_ELIDE_SKIPPED_COPIES)
     return fail(RA_ERR_INVALID_ARG, "copy elision does not apply to the full ring");

@@ -95,9 +95,11 @@ def workloads() -> dict:
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16, nearest-even; returns uint16 bit patterns."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16) & 0xFFFF
+    u = x.view(np.uint32)
+    r = (u >> 16) & np.uint32(1)          # 32-bit arithmetic: a carry past bit 31 only
+    r += u                                # wraps where the 64-bit form would drop it
+    r += np.uint32(0x7FFF)                # under the & 0xFFFF of the top half
+    r >>= 16
     return r.astype(np.uint16)
 
 

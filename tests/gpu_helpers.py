@@ -93,6 +93,25 @@ def oracle_rows(w, inp, rows):
     return O, lse
 
 
-def report(name, **vals):
+# Every parity check's worst error against its tolerance, collected for the
+# end-of-run summary (tests/conftest.py prints it, so margins are on record
+# even though pytest captures the per-test output).
+MARGINS = []
+
+
+def report(name, tol=None, **vals):
+    """Print a parity result.  With a tolerance (one value for every max_*
+    entry, or a dict of entry -> tolerance) the entry with the largest
+    error/tolerance ratio is recorded in MARGINS."""
     print(f"[parity] {name}: " + ", ".join(f"{k}={v:.3e}" if isinstance(v, float) else f"{k}={v}"
                                          for k, v in vals.items()), flush=True)
+    if tol is None:
+        return
+    tols = tol if isinstance(tol, dict) else {k: tol for k in vals if k.startswith("max")}
+    worst = None
+    for k, t in tols.items():
+        e = float(vals[k])
+        if worst is None or e / t > worst[0] / worst[1]:
+            worst = (e, float(t), k)
+    if worst is not None:
+        MARGINS.append({"name": f"{name} [{worst[2]}]", "err": worst[0], "tol": worst[1]})

@@ -54,12 +54,12 @@ def _oracle_grads(w, inp, q_rows, k_rows, heads_for_kv):
     return dQ, dK, dV
 
 
-def _compare(name, got, want):
+def _compare(name, got, want, tol=TOL_BWD):
     err = float(np.abs(got - want).max())
     rel = float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30))
-    H.report(name, max_abs=err, rel_l2=rel)
+    H.report(name, tol=tol, max_abs=err, rel_l2=rel)
     assert np.all(np.isfinite(got))
-    assert err <= TOL_BWD, (name, err)
+    assert err <= tol, (name, err)
     return err
 
 
@@ -176,7 +176,7 @@ def test_ring_bwd_64k_causal(torch):
     rows = rs.row_sample(w, 1024)
     Os, Ls = H.sampled(O, lse, w, rows)
     O_ref, lse_ref = H.oracle_rows(w, inp, rows)
-    H.report("ring_fwd bwd_64k", max_abs_O=float(np.abs(Os - O_ref).max()),
+    H.report("ring_fwd bwd_64k", tol={"max_abs_O": 2e-2, "max_abs_lse": 1e-3}, max_abs_O=float(np.abs(Os - O_ref).max()),
              max_abs_lse=float(np.abs(Ls - lse_ref).max()))
     assert np.abs(Os - O_ref).max() <= 2e-2 and np.abs(Ls - lse_ref).max() <= 1e-3
     cfg = H.cfg_of(w)
@@ -265,7 +265,7 @@ def test_ring_bwd_64k_closed_form_zero_keys(torch):
         got = dV[:, 0, h].float().cpu().numpy().reshape(S, d)
         err_v = max(err_v, float(np.abs(got - want).max()))
         assert np.all(np.isfinite(got))
-    H.report("ring_bwd bwd_64k K=0 dV (all rows)", max_abs=err_v)
+    H.report("ring_bwd bwd_64k K=0 dV (all rows)", tol=TOL_BWD, max_abs=err_v)
     assert err_v <= TOL_BWD, err_v
 
     rng = np.random.default_rng(9700 + w.cfg)
@@ -288,5 +288,5 @@ def test_ring_bwd_64k_closed_form_zero_keys(torch):
             want[i] = scale * (M @ Vh[kr] - u)
         got = dK[:, 0, h].float().cpu().numpy().reshape(S, d)[ks]
         err_k = max(err_k, float(np.abs(got - want).max()))
-    H.report("ring_bwd bwd_64k K=0 dK (sampled rows)", max_abs=err_k, heads=heads)
+    H.report("ring_bwd bwd_64k K=0 dK (sampled rows)", tol=TOL_BWD, max_abs=err_k, heads=heads)
     assert err_k <= TOL_BWD, err_k

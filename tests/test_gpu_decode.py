@@ -51,7 +51,7 @@ def _check(name, O, lse, O_ref, lse_ref):
     fin = np.isfinite(lse_ref)
     eo = float(np.abs(Og - O_ref).max())
     el = float(np.abs(lg[fin] - lse_ref[fin]).max()) if fin.any() else 0.0
-    H.report(name, max_abs_O=eo, max_abs_lse=el)
+    H.report(name, tol={"max_abs_O": TOL_O, "max_abs_lse": TOL_L}, max_abs_O=eo, max_abs_lse=el)
     assert np.all(np.isfinite(Og))
     assert eo <= TOL_O and el <= TOL_L, (name, eo, el)
 

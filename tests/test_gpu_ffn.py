@@ -58,7 +58,7 @@ def test_block_ffn_small_all_rows(torch, rows, h, f, block_rows):
     want = npref.blockwise_ffn(rs.bf16_bits_to_f32(x), rs.bf16_bits_to_f32(w1), rs.bf16_bits_to_f32(w2))
     got = y.float().cpu().numpy().astype(np.float64)
     err = float(np.abs(got - want).max())
-    H.report(f"block_ffn rows={rows} h={h} f={f} block={block_rows}", max_abs=err)
+    H.report(f"block_ffn rows={rows} h={h} f={f} block={block_rows}", tol=TOL, max_abs=err)
     assert np.all(np.isfinite(got)) and err <= TOL
 
 
@@ -102,5 +102,5 @@ def test_block_ffn_7b_block_sampled(torch):
     for tag, out in (("one block", y), ("blocks of 1024", y2)):
         got = out[idx].float().cpu().numpy().astype(np.float64)
         err = float(np.abs(got - want).max())
-        H.report(f"{w.name} {tag}", max_abs=err, rows=len(rows))
+        H.report(f"{w.name} {tag}", tol=TOL, max_abs=err, rows=len(rows))
         assert np.all(np.isfinite(got)) and err <= TOL

@@ -34,7 +34,7 @@ def _check(name, w, O, lse, O_ref, lse_ref):
     tol_o, tol_l = TOL[w.dtype]
     eo = float(np.abs(O - O_ref).max())
     el = float(np.abs(lse - lse_ref).max())
-    H.report(name, max_abs_O=eo, max_abs_lse=el, rows=O.shape[0])
+    H.report(name, tol={"max_abs_O": tol_o, "max_abs_lse": tol_l}, max_abs_O=eo, max_abs_lse=el, rows=O.shape[0])
     assert np.all(np.isfinite(O)) and np.all(np.isfinite(lse))
     assert eo <= tol_o and el <= tol_l
 
@@ -146,6 +146,24 @@ def test_ring_fwd_tiny_f32_all_rows(torch, name):
     assert stats["compute_steps"] == w.n_hosts and stats["transfers"] == w.n_hosts - 1
 
 
+def _check_residency(w, stats):
+    """Per simulated host the forward holds its query block, its output
+    block, the K/V block being folded and the incoming K/V block -- the 6
+    blocks of [P2] 5.3 (6bch with Hq = Hkv; grouped heads make K/V blocks
+    smaller) -- plus the fp32 numerator O and the m, l rows.  The ring
+    buffers the library holds per host (resident_bytes_per_host) are the
+    receive double buffer (2 slots x K, V) and that fp32 state."""
+    el = 2 if w.dtype == rs.DT_BF16 else 4
+    rows = w.batch * w.heads_q * w.block_len
+    q_blk = rows * w.head_dim * el
+    kv_blk = w.batch * w.heads_kv * w.block_len * w.head_dim * el
+    fp32_state = 4 * (2 * rows + rows * w.head_dim)
+    assert stats["resident_bytes_per_host"] == 4 * kv_blk + fp32_state
+    blocks = q_blk + q_blk + (stats["resident_bytes_per_host"] - fp32_state)   # Q, O out, K/V x 2
+    assert blocks <= 6 * q_blk
+    H.report(f"residency {w.name}", blocks_of_6=blocks / q_blk, fp32_state_bytes=fp32_state)
+
+
 def test_ring_fwd_noncausal_32k(torch):
     w = rs.workloads()["noncausal_32k"]
     inp = H.inputs(w)
@@ -155,6 +173,8 @@ def test_ring_fwd_noncausal_32k(torch):
     O_ref, lse_ref = H.oracle_rows(w, inp, rows)
     _check("ring_fwd noncausal_32k", w, Os, Ls, O_ref, lse_ref)
     assert stats["compute_steps"] == 8 and stats["transfers"] == 7
+    assert stats["copy_kind"] == 1, "ring transfers must run on the DMA engines on MI355X"
+    _check_residency(w, stats)
 
 
 @pytest.mark.timeout(600)
@@ -168,6 +188,7 @@ def test_ring_fwd_causal_256k(torch, name):
     O_ref, lse_ref = H.oracle_rows(w, inp, rows)
     _check(f"ring_fwd {name}", w, Os, Ls, O_ref, lse_ref)
     assert stats["skipped_blocks"] == 0   # host 7 is the last host: nothing above it
+    _check_residency(w, stats)
 
 
 @pytest.mark.timeout(900)

@@ -234,6 +234,30 @@ def test_ring_argument_checks():
                        *([FAKE] * 10), 1 << 40, None, None, ctypes.byref(st)) == L.RA_ERR_UNSUPPORTED
     assert ra.raw_call("ra_ring_bwd", ctypes.byref(_cfg(layout=Z, dims=_dims(block_len=63))),
                        *([FAKE] * 10), 1 << 40, None, None, ctypes.byref(st)) == L.RA_ERR_INVALID_ARG
+    # fp32 causal zigzag is refused by the synchronous checks (not after the
+    # first enqueue): the status is UNSUPPORTED and the stats stay untouched
+    st.kernel_launches = -7
+    assert ra.raw_call("ra_ring_bwd", ctypes.byref(_cfg(layout=Z, mask=1, dims=_dims(block_len=256, dtype=1))),
+                       *([FAKE] * 10), 1 << 40, None, None, ctypes.byref(st)) == L.RA_ERR_UNSUPPORTED
+    assert "bf16" in ra.last_error() and st.kernel_launches == -7
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+def test_ring_bwd_fp32_passes_checks():
+    """fp32 ring backward is supported: with valid arguments the call gets
+    past every check to its first HIP call, which on a machine without a GPU
+    fails with RA_ERR_HIP (never RA_ERR_UNSUPPORTED after enqueueing work).
+    Only run where no GPU is visible: the pointers are fake."""
+    if _gpu_visible():
+        pytest.skip("fake device pointers: run only where no GPU is visible")
+    st = L.RaRingStats()
+    rc = ra.raw_call("ra_ring_bwd", ctypes.byref(_cfg(mask=1, dims=_dims(dtype=1))), *([FAKE] * 10), 1 << 40,
+                     None, None, ctypes.byref(st))
+    assert rc == L.RA_ERR_HIP, (rc, ra.last_error())
 
 
 def test_workspace_size_formula():
