@@ -95,6 +95,15 @@ def load():
     """Load libringattn.so (raises if it has not been built)."""
     global _LIB
     if _LIB is None:
+        # The library must run on the HIP runtime that torch loaded: device
+        # pointers and streams come from torch.  Loaded first, it would pull
+        # in the system runtime, and torch would then load its bundled copy
+        # beside it (it names the runtime without the version suffix), leaving
+        # two runtimes in the process.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         if not os.path.exists(LIB_PATH):
             raise ImportError(
                 f"{LIB_PATH} not found: build it with "
