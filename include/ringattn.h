@@ -347,6 +347,25 @@ ra_status ra_ring_decode(const ra_dims *dims, int32_t n_hosts, const void *q, co
                          const void *V, const int32_t *kv_len, void *O, int32_t o_dtype, float *lse,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/* Allocation-free variant of ra_ring_decode, for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * checks, kernels and results (bit for bit) as ra_ring_decode, without the
+ * workspace: the per-chunk partials live in a fixed 32 MiB device array that
+ * the library holds on every GPU it runs on until the process ends (looked up
+ * once per device, on the first call with that device current; the call
+ * runs on the current device, to which `stream` must belong).  A request
+ * whose partials exceed 32 MiB (ra_decode_workspace_size reports the need)
+ * returns RA_ERR_WORKSPACE before any HIP call.  Every call on one GPU shares
+ * that array: calls that overlap in time on one GPU (concurrent streams, or
+ * host threads without ordering) race and must not be issued; calls ordered
+ * on one stream are safe.  Every partial a call reads is written by the same
+ * call, so nothing needs clearing between calls.  No allocation, free or
+ * allocating library routine is called. */
+ra_status ra_ring_decode_noalloc(const ra_dims *dims, int32_t n_hosts, const void *q, const void *K,
+                                 const void *V, const int32_t *kv_len, void *O, int32_t o_dtype,
+                                 float *lse, void *stream);
+
 /* ---------------------------------------------------------------------
  * Blockwise feedforward of the local block
  * ------------------------------------------------------------------- */

@@ -74,6 +74,7 @@ SIGNATURES = [
     ("ra_decode_workspace_size", c_i32, [P(RaDims), c_i32, P(ctypes.c_size_t)]),
     ("ra_ring_decode", c_i32, [P(RaDims), c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp,
                                ctypes.c_size_t, c_vp]),
+    ("ra_ring_decode_noalloc", c_i32, [P(RaDims), c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp]),
     ("ra_ffn_workspace_size", c_i32, [c_i64, c_i32, c_i32, P(ctypes.c_size_t)]),
     ("ra_block_ffn", c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_i32, c_i64, c_vp, ctypes.c_size_t,
                              c_vp]),

@@ -210,6 +210,18 @@ def ring_decode(dims: Dims, n_hosts: int, q, k, v, kv_len, O, lse, workspace, o_
                                     _stream(stream)), "ra_ring_decode")
 
 
+def ring_decode_noalloc(dims: Dims, n_hosts: int, q, k, v, kv_len, O, lse, o_dtype=None, stream=None):
+    """ra_ring_decode without a workspace (ra_ring_decode_noalloc): the
+    partials live in the library's fixed device array; calls that overlap on
+    one GPU race."""
+    d = dims.c()
+    if o_dtype is None:
+        o_dtype = RA_BF16 if str(O.dtype) == "torch.bfloat16" else RA_F32
+    L.check(L.load().ra_ring_decode_noalloc(ctypes.byref(d), n_hosts, _ptr(q), _ptr(k), _ptr(v), _ptr(kv_len),
+                                            _ptr(O), o_dtype, _ptr(lse), _stream(stream)),
+            "ra_ring_decode_noalloc")
+
+
 def ffn_workspace_size(block_rows: int, h: int, f: int) -> int:
     n = ctypes.c_size_t(0)
     L.check(L.load().ra_ffn_workspace_size(block_rows, h, f, ctypes.byref(n)), "ra_ffn_workspace_size")

@@ -30,6 +30,8 @@
 //  * decode_combine_kernel: one wave per (sequence, query head) merges the
 //    partials of every (host, chunk) in host order and writes O / l and the
 //    LSE.
+#include <mutex>
+
 #include "ra_internal.h"
 #include "ra_tile.h"
 
@@ -289,6 +291,32 @@ static hipError_t launch_decode_t(const DecArgs& a, void* out, float* lse, int o
       hipLaunchKernelGGL((decode_combine_kernel<D, false>), dim3((unsigned)g2), dim3(256), 0, s, a, out, lse);
   }
   return hipGetLastError();
+}
+
+// Partials of the allocation-free decode entry point: a fixed device array
+// that each GPU holds for the life of the process.  Host code never uses the
+// array's name as an address: decode_scratch() looks the device address up
+// once per device and hands that out.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with device `dev` current
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecArgs& a, int head_dim, void* out, float* lse, int out_dtype, hipStream_t s) {

@@ -530,9 +530,9 @@ ra_status ra_decode_workspace_size(const ra_dims* dims, int32_t n_hosts, size_t*
   return RA_OK;
 }
 
-ra_status ra_ring_decode(const ra_dims* dims, int32_t n_hosts, const void* q, const void* K, const void* V,
-                         const int32_t* kv_len, void* O, int32_t o_dtype, float* lse, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+// Shared checks of the two decode entry points (everything but the workspace).
+static ra_status check_decode_call(const ra_dims* dims, int32_t n_hosts, const void* q, const void* K, const void* V,
+                            const int32_t* kv_len, const void* O, int32_t o_dtype, const float* lse) {
   RA_CHECK(check_decode(dims, n_hosts));
   if (o_dtype != RA_BF16 && o_dtype != RA_F32) return fail(RA_ERR_INVALID_ARG, "unknown o_dtype %d", o_dtype);
   RA_CHECK(check_ptr(q, "q"));
@@ -543,17 +543,18 @@ ra_status ra_ring_decode(const ra_dims* dims, int32_t n_hosts, const void* q, co
   RA_CHECK(check_ptr(O, "O"));
   if (!lse) return fail(RA_ERR_INVALID_ARG, "lse is NULL");
   if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(RA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
-  RA_CHECK(check_ptr(workspace, "workspace"));
-  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(RA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  return RA_OK;
+}
+
+// Enqueue the decode kernels with their partials at `ws` (layout decode_ws).
+static ra_status decode_enqueue(const ra_dims* dims, int32_t n_hosts, const void* q, const void* K, const void* V,
+                         const int32_t* kv_len, void* O, int32_t o_dtype, float* lse, char* ws, void* stream) {
   const DecWs w = decode_ws(dims, n_hosts);
-  if (workspace_bytes < w.total)
-    return fail(RA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, w.total);
   ra::DecArgs a{};
   a.q = q;
   a.k = K;
   a.v = V;
   a.kv_len = kv_len;
-  char* ws = static_cast<char*>(workspace);
   a.part_m = reinterpret_cast<float*>(ws + w.m);
   a.part_l = reinterpret_cast<float*>(ws + w.l);
   a.part_o = reinterpret_cast<float*>(ws + w.o);
@@ -567,6 +568,32 @@ ra_status ra_ring_decode(const ra_dims* dims, int32_t n_hosts, const void* q, co
   RA_HIP(ra::launch_decode(a, dims->head_dim, O, lse, o_dtype == RA_BF16 ? 0 : 1, (hipStream_t)stream),
          "decode launch");
   return RA_OK;
+}
+
+ra_status ra_ring_decode(const ra_dims* dims, int32_t n_hosts, const void* q, const void* K, const void* V,
+                         const int32_t* kv_len, void* O, int32_t o_dtype, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  RA_CHECK(check_decode_call(dims, n_hosts, q, K, V, kv_len, O, o_dtype, lse));
+  RA_CHECK(check_ptr(workspace, "workspace"));
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(RA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  const DecWs w = decode_ws(dims, n_hosts);
+  if (workspace_bytes < w.total)
+    return fail(RA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, w.total);
+  return decode_enqueue(dims, n_hosts, q, K, V, kv_len, O, o_dtype, lse, static_cast<char*>(workspace), stream);
+}
+
+ra_status ra_ring_decode_noalloc(const ra_dims* dims, int32_t n_hosts, const void* q, const void* K,
+                                 const void* V, const int32_t* kv_len, void* O, int32_t o_dtype, float* lse,
+                                 void* stream) {
+  RA_CHECK(check_decode_call(dims, n_hosts, q, K, V, kv_len, O, o_dtype, lse));
+  const DecWs w = decode_ws(dims, n_hosts);
+  if (w.total > ra::kDecodeScratchBytes)
+    return fail(RA_ERR_WORKSPACE,
+                "decode partials need %zu bytes; the built-in scratch holds %zu (use ra_ring_decode with a workspace)",
+                w.total, ra::kDecodeScratchBytes);
+  void* ws = nullptr;
+  RA_HIP(ra::decode_scratch(&ws), "decode scratch address");
+  return decode_enqueue(dims, n_hosts, q, K, V, kv_len, O, o_dtype, lse, static_cast<char*>(ws), stream);
 }
 
 // Feedforward workspace: the GELU output of one row block (bf16), then the

@@ -105,5 +105,9 @@ hipError_t launch_gemm_nt(const void* A, const void* B, void* C, float* part, si
 size_t gemm_partial_bytes(int M, int N, int K);
 // decode split + combine; out [batch][hq][d] in out_dtype (0 bf16, 1 fp32), lse [batch][hq]
 hipError_t launch_decode(const DecArgs& a, int head_dim, void* out, float* lse, int out_dtype, hipStream_t s);
+// Size of the static device array behind the allocation-free decode call, and
+// its address on the current device (looked up once per device).
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+hipError_t decode_scratch(void** ptr);
 
 }  // namespace ra
