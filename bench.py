@@ -266,10 +266,20 @@ def elementwise_bw(torch, ra, reps=10):
     fin_bytes = rows * (6 * d + 12)     # O fp32 read, m, l read, bf16 out, lse out
     mer_bytes = rows * (12 * d + 12)    # two fp32 O in, one out, three lse
     pre_bytes = rows * (4 * d + 4)      # bf16 O and dO in, D out
-    return {"finalize": {"s": tf, "GBs": fin_bytes / tf / 1e9, "bytes_per_row": 6 * d + 12},
-            "merge": {"s": tm, "GBs": mer_bytes / tm / 1e9, "bytes_per_row": 12 * d + 12},
-            "bwd_preprocess": {"s": tp, "GBs": pre_bytes / tp / 1e9, "bytes_per_row": 4 * d + 4},
-            "peak_GBs": PEAK_HBM_GBS}
+    # reference: torch's device copy of the same O array (read + write), the
+    # plain read/write stream these kernels are measured beside
+    src = O.view(torch.uint8)
+    dst = torch.empty_like(src)
+    tc = timeit(lambda: dst.copy_(src))
+    del src, dst
+    out = {}
+    for key, t, nbytes, per_row in (("finalize", tf, fin_bytes, 6 * d + 12), ("merge", tm, mer_bytes, 12 * d + 12),
+                                     ("bwd_preprocess", tp, pre_bytes, 4 * d + 4)):
+        out[key] = {"s": t, "GBs": nbytes / t / 1e9, "bytes_per_row": per_row,
+                    "frac_hbm_peak": nbytes / t / 1e9 / PEAK_HBM_GBS}
+    out["reference_copy_GBs"] = 2 * O.numel() * 4 / tc / 1e9
+    out["peak_GBs"] = PEAK_HBM_GBS
+    return out
 
 
 def reference_gemm(torch, n=8192, reps=20):

@@ -68,6 +68,19 @@ __device__ inline int xcd_remap_b(int L, int T) {
   return (L % 8) * (T / 8) + (L / 8);
 }
 
+// 16-byte chunk (of 8 d values) that lane group g contributes at d step kk
+// of a 16x16x32 contraction over d.  The order of the d values inside a
+// contraction is free as long as both operands use it.  For tiles read both
+// by rows and by transposing reads (the kSwz16 layout of ra_tile.h), the row
+// reads are bank-conflict free at d = 128 when each lane group takes four
+// consecutive chunks (chunk kk + 4g; measured on gfx950: 2.5 against 3.8 ns
+// per 1 KB wave read with chunk 4kk + g); d = 64 keeps chunk 4kk + g.
+template <int D>
+__device__ inline int dchunk(int kk, int g) {
+  if constexpr (D == 128) return kk + (D / 32) * g;
+  else return 4 * kk + g;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -109,15 +122,16 @@ void dkdv_kernel(BwdArgs a) {
   const __amdgpu_buffer_rsrc_t rv = rsrc(reinterpret_cast<const __bf16*>(a.v) + kvoff, blk_bytes);
 
   // K^T and V^T fragments (B operands of S and dP): sub-tile ks, d step kk,
-  // lane (g, i) holds d 32kk + 8g .. +7 of key kw0 + 16ks + i.
+  // lane (g, i) holds chunk dchunk(kk, g) (d values 8 dchunk .. +7) of key
+  // kw0 + 16ks + i, the chunk the Q and dO row reads deliver to that lane.
   bf16x8 kf[2][NKK], vf[2][NKK];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const int kr = kw0 + 16 * ks + l16;
-      kf[ks][kk] = as_bf16x8(bload16(rk, (kr * D + 32 * kk + 8 * g) * 2));
-      vf[ks][kk] = as_bf16x8(bload16(rv, (kr * D + 32 * kk + 8 * g) * 2));
+      kf[ks][kk] = as_bf16x8(bload16(rk, (kr * D + 8 * dchunk<D>(kk, g)) * 2));
+      vf[ks][kk] = as_bf16x8(bload16(rv, (kr * D + 8 * dchunk<D>(kk, g)) * 2));
     }
   // dK, dV accumulators: sub-tile ks, d tile nt; value r of lane (g, i) is
   // key kw0 + 16ks + 4g + r, d column 16nt + i.  They start from the partial
@@ -225,146 +239,215 @@ void dkdv_kernel(BwdArgs a) {
   // Transposing reads: d tile nt at tile rows 0.. (see STile::tr16_off).
   int roff[NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) roff[kk] = l16 * T::ROWB + (((4 * kk + g) ^ tile::swz<D, tile::kSwz16>(l16)) * 16);
+  for (int kk = 0; kk < NKK; ++kk) roff[kk] = l16 * T::ROWB + ((dchunk<D>(kk, g) ^ tile::swz<D, tile::kSwz16>(l16)) * 16);
   int toff[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) toff[nt] = T::tr16_off(16 * nt, lane);
 
   const float c2 = a.scale_log2;
-  // One query tile (64 rows = 4 MFMA row tiles mt) against this wave's 32
-  // keys, with v_mfma_f32_16x16x32_bf16.  Phases, in issue order:
+  // Work on one query tile (64 rows = 4 MFMA row tiles mt) against this
+  // wave's 32 keys, with v_mfma_f32_16x16x32_bf16, in three kinds of slots:
   //  A  S = Q K^T and dP = dO V^T: slot u = (mt, kk) reads one Q row operand
   //     and one dO row operand and feeds four MFMAs (both key sub-tiles);
-  //  B  P = 2^(S c2 - lse2), dS = P (dP - D): the 16 values of query rows
-  //     0..31 (half 0) run beside the MFMAs of rows 32..63, those of half 1
-  //     beside the first dV/dK MFMAs (which use half 0 only);
+  //  P  P = 2^(S c2 - lse2), dS = P (dP - D): the 16 values of query rows
+  //     0..31 (half 0) need row tiles 0, 1 of A; those of half 1 row tiles 2, 3;
   //  C  dV += P^T dO, dK += dS^T Q over query steps kq (32 rows = half kq):
   //     slot v = (kq, nt) reads the transposed dO and Q operands and feeds
   //     four MFMAs.  P^T's item j of lane (g, i) is query 32kq + 16(j/4) +
   //     4g + j%4, the order in which the transposing reads deliver dO and Q.
-  // Operand reads run kPre slots ahead, pinned by sched_barrier.
-  int delta = sd[0];                                       // the current segment's offset
-  auto compute = [&](int it, auto masked) {
-    int q0, hg_unused;
-    tile_of(it, q0, hg_unused);
-    const unsigned char* base = smem + (it % NS) * BUF;
-    const unsigned char* qs = base;
-    const unsigned char* os = base + T::BYTES;
-    const float* lsep = reinterpret_cast<const float*>(base + 2 * T::BYTES);
-    const float* dp = lsep + kTile;
-    f32x4 s[4][2], dpv[4][2];
+  // The tiles run as a software pipeline so that every MFMA has softmax work
+  // beside it: iteration t issues A of tile t and C of tile t-1 in
+  // alternating slots, the softmax of tile t-1's half 1 beside the first
+  // half of the slots (C of half 1 comes after it) and that of tile t's
+  // half 0 beside the second half (A of row tiles 0, 1 is done by then).
+  // S/dP row tiles and the P/dS halves are reused in place: each is read
+  // before the slot that overwrites it.  Tile t-1's LDS stage stays in use
+  // until iteration t ends, so the DMA ring keeps two tiles in flight.
+  constexpr int ND = 4 * NKK;                              // A slots = C slots per tile
+  static_assert(ND == 2 * NT, "A and C phases have one slot count");
+  static_assert(NS >= 3, "the pipeline holds two stages besides the ones in flight");
+  constexpr int EH = 16 / (ND / 2);                        // softmax values per slot pair
+  constexpr int kPre = RA_DKDV_PREFETCH;
+  f32x4 s[4][2], dpv[4][2];
+  bf16x8 pa[2][2], dsa[2][2];                              // [ks][kq]
+  f32x4 la[4], da[4];                                      // lse (base 2) and D of row tile mt
+  bf16x8 qa[ND], oa[ND], ob[ND], qb[ND];
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  auto stage = [&](int it) -> const unsigned char* { return smem + (it % NS) * BUF; };
+  auto a_read = [&](const unsigned char* qs, int u) {
+    const int mt = u / NKK, kk = u % NKK;
+    qa[u] = *reinterpret_cast<const bf16x8*>(qs + 16 * mt * T::ROWB + roff[kk]);
+    oa[u] = *reinterpret_cast<const bf16x8*>(qs + T::BYTES + 16 * mt * T::ROWB + roff[kk]);
+  };
+  auto c_read = [&](const unsigned char* qs, int v) {
+    const int kq = v / NT, nt = v % NT;
+    ob[v] = T::tr_at(qs + T::BYTES + 32 * kq * T::ROWB, toff[nt], toff[nt] + 16 * T::ROWB);
+    qb[v] = T::tr_at(qs + 32 * kq * T::ROWB, toff[nt], toff[nt] + 16 * T::ROWB);
+  };
+  // lse (base 2) and D of query rows 16mt + 4g + 0..3, one typed vector load
+  // each (keeps the load's alias information, see ra_tile.h)
+  auto ld_read = [&](const unsigned char* qs, int mt) {
+    const float* lsep = reinterpret_cast<const float*>(qs + 2 * T::BYTES);
+    la[mt] = *reinterpret_cast<const f32x4*>(lsep + 16 * mt + 4 * g) * kBwdLog2e;
+    da[mt] = *reinterpret_cast<const f32x4*>(lsep + kTile + 16 * mt + 4 * g);
+  };
+  auto a_mfma = [&](int u) {
+    const int mt = u / NKK, kk = u % NKK;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          s[mt][ks][r] = 0.f;
-          dpv[mt][ks][r] = 0.f;
-        }
-    constexpr int NU = 4 * NKK, NC = 2 * NT, kPre = RA_DKDV_PREFETCH;
-    bf16x8 qa[NU], oa[NU], ob[NC], qb[NC];
-    auto a_read = [&](int u) {
-      const int mt = u / NKK, kk = u % NKK;
-      qa[u] = *reinterpret_cast<const bf16x8*>(qs + 16 * mt * T::ROWB + roff[kk]);
-      oa[u] = *reinterpret_cast<const bf16x8*>(os + 16 * mt * T::ROWB + roff[kk]);
-    };
-    auto c_read = [&](int v) {
-      const int kq = v / NT, nt = v % NT;
-      ob[v] = T::tr_at(os + 32 * kq * T::ROWB, toff[nt], toff[nt] + 16 * T::ROWB);
-      qb[v] = T::tr_at(qs + 32 * kq * T::ROWB, toff[nt], toff[nt] + 16 * T::ROWB);
-    };
-    // lse (base 2) and D of query rows 16mt + 4g + 0..3, one typed vector load
-    // each (keeps the load's alias information, see ra_tile.h)
-    f32x4 la[4], da[4];
-    auto ld_read = [&](int mt) {
-      la[mt] = *reinterpret_cast<const f32x4*>(lsep + 16 * mt + 4 * g) * kBwdLog2e;
-      da[mt] = *reinterpret_cast<const f32x4*>(dp + 16 * mt + 4 * g);
-    };
-    // value e of half hf: sub-tile ks = e / 8, row tile mt = 2hf + (e / 4) % 2,
-    // r = e % 4; it lands in item 4 ((e / 4) % 2) + r of pa/dsa[ks][hf].
-    // (Every row of an unmasked tile sees a key, so its lse is finite; in a
-    // masked tile invisible pairs, including all pairs of a row that sees no
-    // key at all, get P = 0 by selection.)
-    bf16x8 pa[2][2], dsa[2][2];
-    auto softmax_elem = [&](int hf, int e) {
-      const int ks = e >> 3, mh = (e >> 2) & 1, r = e & 3, mt = 2 * hf + mh;
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][ks][r], c2, -la[mt][r]));
-      if constexpr (decltype(masked)::value) {
-        const int key = kw0 + 16 * ks + l16;
-        const int qrow = q0 + 16 * mt + 4 * g + r;
-        const bool vis = (key < c) & (qrow < c) & visible(key - qrow, delta);
-        p = vis ? p : 0.f;
-      }
-      pa[ks][hf][4 * mh + r] = (__bf16)p;
-      dsa[ks][hf][4 * mh + r] = (__bf16)(p * (dpv[mt][ks][r] - da[mt][r]));
-    };
-    constexpr int EA = 16 / (NU / 2), EC = 16 / (NC / 2);   // softmax values per slot
-    static_assert(EA * (NU / 2) == 16 && EC * (NC / 2) == 16, "slots must divide a half's 16 values");
-
-#pragma unroll
-    for (int u = 0; u < kPre; ++u) a_read(u);
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      if (u + kPre < NU) a_read(u + kPre);
-      else c_read(u + kPre - NU);
-      if (u == 0) { ld_read(0); ld_read(1); }
-      if (u == NU / 2) { ld_read(2); ld_read(3); }
-      const int mt = u / NKK, kk = u % NKK;
-      s[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[u], kf[0][kk], s[mt][0], 0, 0, 0);
-      s[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[u], kf[1][kk], s[mt][1], 0, 0, 0);
-      dpv[mt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa[u], vf[0][kk], dpv[mt][0], 0, 0, 0);
-      dpv[mt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa[u], vf[1][kk], dpv[mt][1], 0, 0, 0);
-      if (u >= NU / 2) {                         // half 0 (row tiles 0, 1) is complete
-#pragma unroll
-        for (int e = 0; e < EA; ++e) softmax_elem(0, (u - NU / 2) * EA + e);
-      }
-      __builtin_amdgcn_sched_barrier(0);         // keep each slot's reads kPre slots ahead
+    for (int ks = 0; ks < 2; ++ks) {
+      s[mt][ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[u], kf[ks][kk], kk == 0 ? zero4 : s[mt][ks], 0, 0, 0);
+      dpv[mt][ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa[u], vf[ks][kk], kk == 0 ? zero4 : dpv[mt][ks], 0, 0, 0);
     }
+  };
+  auto c_mfma = [&](int v) {
+    const int kq = v / NT, nt = v % NT;
 #pragma unroll
-    for (int v = 0; v < NC; ++v) {
-      if (v + kPre < NC) c_read(v + kPre);
-      const int kq = v / NT, nt = v % NT;
-      acc_dv[0][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[0][kq], ob[v], acc_dv[0][nt], 0, 0, 0);
-      acc_dv[1][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[1][kq], ob[v], acc_dv[1][nt], 0, 0, 0);
-      acc_dk[0][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsa[0][kq], qb[v], acc_dk[0][nt], 0, 0, 0);
-      acc_dk[1][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsa[1][kq], qb[v], acc_dk[1][nt], 0, 0, 0);
-      if (v < NC / 2) {                          // slots of kq = 0: half 1's softmax beside them
+    for (int ks = 0; ks < 2; ++ks) {
+      acc_dv[ks][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[ks][kq], ob[v], acc_dv[ks][nt], 0, 0, 0);
+      acc_dk[ks][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsa[ks][kq], qb[v], acc_dk[ks][nt], 0, 0, 0);
+    }
+  };
+  // value e of half hf of the tile whose first query row is q0, under the
+  // visibility offset dl: sub-tile ks = e / 8, row tile mt = 2hf + (e / 4) % 2,
+  // r = e % 4; it lands in item 4 ((e / 4) % 2) + r of pa/dsa[ks][hf].
+  // (Every row of an unmasked tile sees a key, so its lse is finite; in a
+  // masked tile invisible pairs, including all pairs of a row that sees no
+  // key at all, get P = 0 by selection.)
+  auto softmax_elem = [&](int hf, int e, int q0, int dl, auto masked) {
+    const int ks = e >> 3, mh = (e >> 2) & 1, r = e & 3, mt = 2 * hf + mh;
+    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][ks][r], c2, -la[mt][r]));
+    if constexpr (decltype(masked)::value) {
+      const int key = kw0 + 16 * ks + l16;
+      const int qrow = q0 + 16 * mt + 4 * g + r;
+      const bool vis = (key < c) & (qrow < c) & visible(key - qrow, dl);
+      p = vis ? p : 0.f;
+    }
+    pa[ks][hf][4 * mh + r] = (__bf16)p;
+    dsa[ks][hf][4 * mh + r] = (__bf16)(p * (dpv[mt][ks][r] - da[mt][r]));
+  };
+
+  // first tile: A with the softmax of half 0 beside its second half
+  auto prologue = [&](int it, int q0, int dl, auto masked) {
+    const unsigned char* qs = stage(it);
+    ld_read(qs, 0);
+    ld_read(qs, 1);
 #pragma unroll
-        for (int e = 0; e < EC; ++e) softmax_elem(1, v * EC + e);
+    for (int u = 0; u < kPre; ++u) a_read(qs, u);
+#pragma unroll
+    for (int u = 0; u < ND; ++u) {
+      if (u + kPre < ND) a_read(qs, u + kPre);
+      a_mfma(u);
+      if (u >= ND / 2) {
+#pragma unroll
+        for (int e = 0; e < EH; ++e) softmax_elem(0, (u - ND / 2) * EH + e, q0, dl, masked);
+      }
+      if (u == ND / 2) {
+        ld_read(qs, 2);
+        ld_read(qs, 3);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto step = [&](int it, auto masked) {
-    if (it + NS - 1 < n_iter) issue(it + NS - 1);        // into the stage read in iteration it - 1
-    if constexpr (decltype(masked)::value) {
-      // keys [kw0, kw0+32) against queries [q0, q0+64): skip when none is visible
-      int q0, hg_unused;
-      tile_of(it, q0, hg_unused);
-      if ((kw0 < c) && visible(kw0 - (q0 + kTile - 1), delta)) compute(it, masked);
-    } else {
-      compute(it, masked);
+  // iteration t: A of tile t and C of tile t-1 in alternating slots
+  auto body = [&](int it, int q0, int dl, int q0p, int dlp, auto mprev, auto masked) {
+    const unsigned char* qs = stage(it);
+    const unsigned char* qp = stage(it - 1);
+    ld_read(qs, 0);
+    ld_read(qs, 1);
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) {
+      a_read(qs, j);
+      c_read(qp, j);
     }
-    if (it + 1 < n_iter) wait_tile(it + 1, min(it + NS - 1, n_iter - 1));
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < ND; ++j) {
+      if (j + kPre < ND) {
+        a_read(qs, j + kPre);
+        c_read(qp, j + kPre);
+      }
+      a_mfma(j);
+      c_mfma(j);
+      if (j < ND / 2) {
+#pragma unroll
+        for (int e = 0; e < EH; ++e) softmax_elem(1, j * EH + e, q0p, dlp, mprev);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EH; ++e) softmax_elem(0, (j - ND / 2) * EH + e, q0, dl, masked);
+      }
+      if (j == ND / 2 - 1) {                   // tile t-1's half 1 is done with la/da[2, 3]
+        ld_read(qs, 2);
+        ld_read(qs, 3);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // last tile: C with the softmax of half 1 beside its first half
+  auto epilogue = [&](int it, int q0, int dl, auto masked) {
+    const unsigned char* qs = stage(it);
+#pragma unroll
+    for (int v = 0; v < kPre; ++v) c_read(qs, v);
+#pragma unroll
+    for (int v = 0; v < ND; ++v) {
+      if (v + kPre < ND) c_read(qs, v + kPre);
+      if (v < ND / 2) {
+#pragma unroll
+        for (int e = 0; e < EH; ++e) softmax_elem(1, v * EH + e, q0, dl, masked);
+      }
+      c_mfma(v);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
 #pragma unroll
-  for (int i = 0; i < NS - 1; ++i)
+  for (int i = 0; i < NS - 2; ++i)
     if (i < n_iter) issue(i);
-  if (n_iter > 0) wait_tile(0, min(NS - 2, n_iter - 1));
+  if (n_iter > 0) wait_tile(0, min(NS - 3, n_iter - 1));
   __syncthreads();
   // Query tiles run in order (heads of the group innermost); a tile needs no
   // per-element mask when every pair of this workgroup is visible and in
-  // range.  Masked head, unmasked middle and masked tail of each segment run
-  // as separate loops so the accumulators keep their registers.
-#pragma unroll
+  // range.  The unmasked middle of each segment runs as the pipeline above;
+  // the masked tiles of the diagonal band and of a ragged last tile (a few per
+  // workgroup) run one at a time (A, then C) and are skipped by a wave none
+  // of whose pairs is visible.  Iteration `it` refills the stage last read in
+  // iteration it - 1 and ends with tile it + 1 landed.
+  auto next = [&](int it) {
+    if (it + 1 < n_iter) wait_tile(it + 1, min(it + NS - 2, n_iter - 1));
+    __syncthreads();
+  };
   for (int sg = 0; sg < 2; ++sg) {
-    delta = sd[sg];
-    for (int it = ib[sg]; it < iu[sg]; ++it) step(it, std::true_type{});
-    for (int it = iu[sg]; it < itl[sg]; ++it) step(it, std::false_type{});
-    for (int it = itl[sg]; it < ib[sg + 1]; ++it) step(it, std::true_type{});
+    const int dl = sg ? sd[1] : sd[0];
+    const int seg_b = sg ? ib[1] : ib[0], seg_u = sg ? iu[1] : iu[0];
+    const int seg_t = sg ? itl[1] : itl[0], seg_e = sg ? ib[2] : ib[1];
+    auto masked_run = [&](int b, int e) {
+      for (int it = b; it < e; ++it) {
+        if (it + NS - 2 < n_iter) issue(it + NS - 2);
+        int q0, hg_unused;
+        tile_of(it, q0, hg_unused);
+        if ((kw0 < c) && visible(kw0 - (q0 + kTile - 1), dl)) {
+          prologue(it, q0, dl, std::true_type{});
+          epilogue(it, q0, dl, std::true_type{});
+        }
+        next(it);
+      }
+    };
+    masked_run(seg_b, seg_u);
+    if (seg_u < seg_t) {
+      int q0p, hg_unused;
+      tile_of(seg_u, q0p, hg_unused);
+      if (seg_u + NS - 2 < n_iter) issue(seg_u + NS - 2);
+      prologue(seg_u, q0p, dl, std::false_type{});
+      for (int it = seg_u + 1; it < seg_t; ++it) {
+        next(it - 1);
+        if (it + NS - 2 < n_iter) issue(it + NS - 2);
+        int q0;
+        tile_of(it, q0, hg_unused);
+        body(it, q0, dl, q0p, dl, std::false_type{}, std::false_type{});
+        q0p = q0;
+      }
+      epilogue(seg_t - 1, q0p, dl, std::false_type{});
+      next(seg_t - 1);
+    }
+    masked_run(seg_t, seg_e);
   }
 
   // epilogue: out = (in + contribution) (scale on dK), the accumulators
@@ -476,7 +559,9 @@ void dq_kernel(BwdArgs a) {
   float* dqp = a.dq + qoff;
 
   // Q^T and dO^T fragments (B operands of S^T and dP^T): sub-tile qs, d step
-  // kk, lane (g, i) holds d 32kk + 8g .. +7 of row qw0 + 16qs + i; that row's
+  // kk, lane (g, i) holds, of row qw0 + 16qs + i, chunk dchunk(kk, g) of Q
+  // (the chunk the K row reads deliver) and d 32kk + 8g .. +7 of dO (V is
+  // staged with the row-read swizzle and read in that order); that row's
   // lse (base 2; +inf for a row without keys, so P = 0) and D.
   bf16x8 qf[2][NKK], of[2][NKK];
   float lse2[2], Dq[2];
@@ -485,7 +570,7 @@ void dq_kernel(BwdArgs a) {
     const int qr = qw0 + 16 * qs + l16;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      qf[qs][kk] = as_bf16x8(bload16(rq, (qr * D + 32 * kk + 8 * g) * 2));
+      qf[qs][kk] = as_bf16x8(bload16(rq, (qr * D + 8 * dchunk<D>(kk, g)) * 2));
       of[qs][kk] = as_bf16x8(bload16(ro, (qr * D + 32 * kk + 8 * g) * 2));
     }
     lse2[qs] = INFINITY;
@@ -511,7 +596,7 @@ void dq_kernel(BwdArgs a) {
   int roff[NKK], rvoff[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
-    roff[kk] = l16 * T::ROWB + (((4 * kk + g) ^ tile::swz<D, tile::kSwz16>(l16)) * 16);
+    roff[kk] = l16 * T::ROWB + ((dchunk<D>(kk, g) ^ tile::swz<D, tile::kSwz16>(l16)) * 16);
     rvoff[kk] = l16 * T::ROWB + (((4 * kk + g) ^ tile::swz<D, tile::kSwzRow>(l16)) * 16);
   }
   int toff[NT];

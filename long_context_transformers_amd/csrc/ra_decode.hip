@@ -105,10 +105,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
   auto dma_tile = [&](int t, int stage) {
     unsigned char* st = smem + stage * STAGE;
     const int row0 = k_begin + t * kDecTile;
-    SK::dma(rk, st, row0, wave, lane);
-    SK::dma(rk, st + SK::BYTES, row0 + 64, wave, lane);
-    SV::dma(rv, st + 2 * SK::BYTES, row0, wave, lane);
-    SV::dma(rv, st + 3 * SK::BYTES, row0 + 64, wave, lane);
+    SK::template dma<tile::kStream>(rk, st, row0, wave, lane);             // each cached row is read once
+    SK::template dma<tile::kStream>(rk, st + SK::BYTES, row0 + 64, wave, lane);
+    SV::template dma<tile::kStream>(rv, st + 2 * SK::BYTES, row0, wave, lane);
+    SV::template dma<tile::kStream>(rv, st + 3 * SK::BYTES, row0 + 64, wave, lane);
   };
   auto allmax = [](float x) {
     auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);

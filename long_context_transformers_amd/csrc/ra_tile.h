@@ -27,9 +27,12 @@ __device__ inline uint4 bload16(__amdgpu_buffer_rsrc_t r, int byte_off) {
 }
 __device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 // 16-byte LDS-DMA load: lane L's 16 bytes from r + voff land at lds + 16 L.
+// kCachePolicy 2 marks the load non-temporal (data read exactly once).
+template <int kCachePolicy = 0>
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, kCachePolicy);
 }
+constexpr int kStream = 2;   // non-temporal cache policy of the buffer loads
 __device__ inline void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most N vector-memory instructions of this wave are in flight.
 template <int N>
@@ -92,13 +95,14 @@ struct STile {
   // instruction i writes LDS bytes [(wave*DPW + i) * 1024, +1024); lane L
   // lands on row R = idx / CPR, chunk C = idx % CPR (idx = (wave*DPW + i)*64
   // + L) and fetches global chunk C ^ swz(R).
+  template <int kCachePolicy = 0>
   __device__ static void dma(__amdgpu_buffer_rsrc_t r, unsigned char* lds, int row0, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < DPW; ++i) {
       const int ins = wave * DPW + i;
       const int R = ins * RPI + lane / CPR;
       const int C = lane % CPR;
-      dma16(r, lds + ins * 1024, (row0 + R) * ROWB + ((C ^ swz<D, V>(R)) * 16));
+      dma16<kCachePolicy>(r, lds + ins * 1024, (row0 + R) * ROWB + ((C ^ swz<D, V>(R)) * 16));
     }
   }
   // 16-byte row read: global chunk c of row R.
