@@ -305,21 +305,25 @@ def reference_gemm(torch, n=8192, reps=20):
             "ms": ms}
 
 
-def causal_rates(torch, ra, steps=3):
-    """Forward TFLOP/s of the causal 256K host-7 workload in the contiguous,
-    striped and zigzag layouts and of the 786K striped GQA host-15 workload
-    (seeded device-side inputs)."""
+def causal_rates(torch, ra, steps=2):
+    """One host's share of the causal 256K workload (host 7; contiguous,
+    striped and zigzag layouts) and of the 786K striped GQA workload (host
+    15): ring forward and ring backward of that host (seeded device-side
+    inputs), TFLOP/s over the host's visible pairs (4 d forward, 10 d
+    backward) from the per-step kernel times, and the whole-call time."""
     out = {}
     wl = rs.workloads()
     for key in ("causal_256k_contig", "causal_256k_striped", "causal_256k_zigzag", "striped_786k_gqa"):
         w = wl[key]
-        ring = Ring(w, torch, ra, seed=w.cfg)
+        ring = Ring(w, torch, ra, seed=w.cfg, with_bwd=True)
         ring.fwd()
+        ring.bwd()
         torch.cuda.synchronize()
-        wall, gpu_ms, f_ms, _ = time_ring(ring, steps, 0, False)
-        fl = counted_flops(w, 4)
-        out[key] = {"ms": gpu_ms / steps, "tflops": fl / (gpu_ms / steps / 1e3) / 1e12,
-                    "kernel_ms_per_step": sum(f_ms) / steps}
+        wall, gpu_ms, f_ms, b_ms = time_ring(ring, steps, 0, True)
+        f_pass, b_pass = sum(f_ms) / steps, sum(b_ms) / steps
+        out[key] = {"fwd_ms": f_pass, "fwd_tflops": counted_flops(w, 4) / (f_pass / 1e3) / 1e12,
+                    "bwd_ms": b_pass, "bwd_tflops": counted_flops(w, 10) / (b_pass / 1e3) / 1e12,
+                    "gpu_event_ms_per_step": gpu_ms / steps}
         del ring
         torch.cuda.empty_cache()
     return out
@@ -638,7 +642,7 @@ def main():
             extra["striped_vs_noncausal_per_flop"] = {
                 "fwd": rates["fwd_kernel_tflops"] / nc["fwd_kernel_tflops"],
                 "bwd": rates["bwd_step_tflops"] / nc["bwd_step_tflops"]}
-        log("[bench] one host's share: causal 256K (contiguous, striped, zigzag) and 786K striped GQA forward")
+        log("[bench] one host's share: causal 256K (contiguous, striped, zigzag) and 786K striped GQA forward + backward")
         extra["causal"] = causal_rates(torch, ra)
         log("[bench] causal 64K forward + backward")
         extra["causal_bwd"] = bwd_rates(torch, ra)

@@ -291,7 +291,9 @@ ra_status ra_ring_fwd(const ra_ring_cfg *cfg, const void *Q, const void *K, cons
                       void *O, float *lse, void *workspace, size_t workspace_bytes,
                       void *compute_stream, void *comm_stream, ra_ring_stats *stats);
 
-/* Ring backward for all N hosts (host_begin = 0, host_end = N):
+/* Ring backward ([P2] 5.2: the backward sweeps the ring again and
+ * accumulates dQ, dK, dV from what the forward saved).
+ * All N hosts (host_begin = 0, host_end = N):
  *   Q, O, dO: [N][B][Hq][c][d] (dims->dtype); lse: [N][B][Hq][c] fp32 from
  *   ra_ring_fwd; K, V: [N][B][Hkv][c][d].
  * bf16 inputs run on the MFMA kernels; fp32 inputs (small problems) on plain
@@ -303,7 +305,17 @@ ra_status ra_ring_fwd(const ra_ring_cfg *cfg, const void *Q, const void *K, cons
  * accumulators travel with their block: the step kernel adds its
  * contribution to the partial sum received from host h-1 and stores the sum
  * straight into host h+1's receive slot (a neighbour store), and after step
- * N-1 that store lands at the block's owner, i.e. in dK/dV. */
+ * N-1 that store lands at the block's owner, i.e. in dK/dV.
+ * A proper subset of hosts (e.g. one host's share, host_end - host_begin = 1):
+ *   Q, O, dO: [na][B][Hq][c][d] and lse: [na][B][Hq][c] of the simulated
+ *   hosts (na = host_end - host_begin); K, V: the pool [N][B][Hkv][c][d].
+ *   dQ: [na][B][Hq][c][d] fp32, complete for the simulated hosts.
+ *   dK, dV: [N][B][Hkv][c][d] fp32, the simulated hosts' contributions to
+ *   every block (a real ring adds them to the running sums that pass
+ *   through; over disjoint host subsets covering the ring they sum to the
+ *   full gradient).  The call clears dQ, dK, dV first.  Blocks come from the
+ *   pool by side-stream copies into the receive slots, as in ra_ring_fwd;
+ *   RA_FLAG_ELIDE_SKIPPED_COPIES omits the copies of blocks a host skips. */
 ra_status ra_ring_bwd(const ra_ring_cfg *cfg, const void *Q, const void *K, const void *V,
                       const void *O, const float *lse, const void *dO, float *dQ, float *dK,
                       float *dV, void *workspace, size_t workspace_bytes, void *compute_stream,

@@ -137,7 +137,9 @@ BwdWs bwd_ws(const ra_ring_cfg* c) {
   const size_t slot = (size_t)na * kv_elems(d) * elem_bytes(d);
   w.rk = off; off = align256(off + 2 * slot);
   w.rv = off; off = align256(off + 2 * slot);
-  const size_t aslot = (size_t)na * kv_elems(d) * sizeof(float);
+  // rotating dK/dV partial sums: only when the whole ring is simulated (a
+  // subset of hosts accumulates its contributions straight into dK/dV)
+  const size_t aslot = na == c->n_hosts ? (size_t)na * kv_elems(d) * sizeof(float) : 0;
   w.dk = off; off = align256(off + 2 * aslot);
   w.dv = off; off = align256(off + 2 * aslot);
   w.total = off;
@@ -296,6 +298,104 @@ ra_status enqueue_transfer(const ra_ring_cfg* cfg, int s, const char* K, const c
 }
 
 }  // namespace
+
+// Ring backward for a proper subset of the hosts, e.g. one host's share:
+// host h holds, at step s, block src = (h - s) mod N (from the pool, copied
+// into its receive slot on `comm` as in the forward), adds its queries'
+// contribution to dQ_h and to block src's dK/dV.  dQ [na][..] is complete
+// for the simulated hosts; dK, dV [N][..] hold the simulated hosts'
+// contributions to every block (with all hosts simulated they would be the
+// full gradient; summed over disjoint host subsets they are).  dQ, dK, dV are
+// cleared first and every block pair accumulates into them, one launch per
+// simulated host and step (the hosts of a step hold different blocks).
+// Arguments were checked by the caller.
+static ra_status ring_bwd_hosts(const ra_ring_cfg* cfg, const void* Q, const void* K, const void* V,
+                                const void* O, const float* lse, const void* dO, float* dQ, float* dK, float* dV,
+                                char* ws, hipStream_t cs, hipStream_t ms, ra_ring_stats* stats) {
+  const ra_dims* d = &cfg->dims;
+  const int N = cfg->n_hosts, hb = cfg->host_begin, na = cfg->host_end - cfg->host_begin;
+  const bool zz = cfg->layout == RA_LAYOUT_ZIGZAG && cfg->mask == RA_MASK_CAUSAL;
+  const BwdWs w = bwd_ws(cfg);
+  float* Dbuf = reinterpret_cast<float*>(ws + w.D);
+  char* rk = ws + w.rk;
+  char* rv = ws + w.rv;
+  const int eb = elem_bytes(d);
+  const size_t blk = (size_t)kv_elems(d) * eb;
+  const int64_t kvn = kv_elems(d);
+  ra_ring_stats st{};
+  std::vector<int> per_host(na, 0);
+  st.resident_bytes_per_host = (int64_t)(4 * blk + sizeof(float) * q_rows(d));
+
+  RingEvents ev;
+  RA_HIP(ev.create(), "event create");
+  RA_HIP(ev.order_comm_after_compute(cs, ms), "order comm after compute");
+  RA_HIP(ra::launch_fill_f32(dQ, 0.f, (int64_t)na * q_elems(d), cs), "clear dQ");
+  RA_HIP(ra::launch_fill_f32(dK, 0.f, (int64_t)N * kvn, cs), "clear dK");
+  RA_HIP(ra::launch_fill_f32(dV, 0.f, (int64_t)N * kvn, cs), "clear dV");
+  RA_HIP(ra::launch_bwd_pre(O, dO, Dbuf, (int64_t)na * q_rows(d), d->head_dim, d->dtype, cs), "bwd_pre launch");
+  st.kernel_launches += 4;
+
+  for (int s = 0; s < N; ++s) {
+    if (s + 1 < N) {
+      if (ms != cs && s >= 1) RA_HIP(hipStreamWaitEvent(ms, ev.used[(s + 1) & 1], 0), "wait used");
+      RA_CHECK(enqueue_transfer(cfg, s, static_cast<const char*>(K), static_cast<const char*>(V), rk, rv, blk, ms,
+                                &st, &per_host));
+      if (ms != cs) RA_HIP(hipEventRecord(ev.recv[(s + 1) & 1], ms), "record recv");
+    }
+    if (ms != cs && s >= 1) RA_HIP(hipStreamWaitEvent(cs, ev.recv[s & 1], 0), "wait recv");
+    if (cfg->step_events) RA_HIP(hipEventRecord((hipEvent_t)cfg->step_events[2 * s], cs), "record step event");
+    bool launched = false;
+    for (int a = 0; a < na; ++a) {
+      const int h = hb + a;
+      ra_step stp;
+      schedule_one(N, h, d->block_len, cfg->layout, cfg->mask, s, &stp);
+      if (stp.cls == RA_BLK_SKIP) {
+        st.skipped_blocks++;
+        continue;
+      }
+      ra::BwdArgs args{};
+      args.q = static_cast<const char*>(Q) + (size_t)a * q_elems(d) * eb;
+      args.k = s == 0 ? static_cast<const char*>(K) + (size_t)h * blk : rk + (size_t)(s & 1) * na * blk + (size_t)a * blk;
+      args.v = s == 0 ? static_cast<const char*>(V) + (size_t)h * blk : rv + (size_t)(s & 1) * na * blk + (size_t)a * blk;
+      args.dO = static_cast<const char*>(dO) + (size_t)a * q_elems(d) * eb;
+      args.lse = lse + (size_t)a * q_rows(d);
+      args.D = Dbuf + (size_t)a * q_rows(d);
+      args.dq = dQ + (size_t)a * q_elems(d);
+      args.dq_accumulate = 1;
+      args.dk_in = args.dk_out = dK + (size_t)stp.src * kvn;
+      args.dv_in = args.dv_out = dV + (size_t)stp.src * kvn;
+      args.dkv_out_host_shift = 0;
+      args.q_host_stride = q_elems(d);
+      args.kv_host_stride = kvn;
+      args.ml_host_stride = q_rows(d);
+      args.dkv_in_host_stride = kvn;
+      args.dkv_out_host_stride = kvn;
+      args.batch = d->batch; args.hq = d->heads_q; args.hkv = d->heads_kv; args.c = d->block_len; args.n_hosts = 1;
+      args.scale = eff_scale(d);
+      args.scale_log2 = args.scale * kLog2e;
+      args.zz_half = zz ? d->block_len / 2 : 0;
+      if (zz) {
+        args.delta[0] = d->block_len;
+        zz_delta4(cfg->mask, N, h, stp.src, d->block_len, args.delta4[0]);
+      } else {
+        args.delta[0] = compute_delta(cfg->mask, stp.q_offset, stp.kv_offset, stp.stride, d->block_len);
+      }
+      hipError_t e = ra::launch_bwd(args, d->head_dim, d->dtype, cs);
+      if (e == hipErrorNotSupported) return fail(RA_ERR_UNSUPPORTED, "ring backward not available for this shape");
+      if (e != hipSuccess) return hip_fail(e, "ring bwd launch");
+      st.kernel_launches += 2;
+      launched = true;
+    }
+    if (launched) st.compute_steps++;
+    if (cfg->step_events) RA_HIP(hipEventRecord((hipEvent_t)cfg->step_events[2 * s + 1], cs), "record step event");
+    if (ms != cs) RA_HIP(hipEventRecord(ev.used[s & 1], cs), "record used");
+  }
+  int mx = 0;
+  for (int v : per_host) mx = std::max(mx, v);
+  st.transfers = mx;
+  if (stats) *stats = st;
+  return RA_OK;
+}
 
 // Decode chunking: enough (host, sequence, KV head, chunk) workgroups to
 // fill the chip (about 2048), chunks a multiple of 128 keys.
@@ -767,13 +867,12 @@ ra_status ra_ring_bwd(const ra_ring_cfg* cfg, const void* Q, const void* K, cons
                       const float* lse, const void* dO, float* dQ, float* dK, float* dV, void* workspace,
                       size_t workspace_bytes, void* compute_stream, void* comm_stream, ra_ring_stats* stats) {
   RA_CHECK(check_cfg(cfg));
-  if (cfg->host_begin != 0 || cfg->host_end != cfg->n_hosts)
-    return fail(RA_ERR_UNSUPPORTED, "ring backward runs every host (host_begin = 0, host_end = n_hosts)");
+  const bool full = cfg->host_begin == 0 && cfg->host_end == cfg->n_hosts;
   const bool zz = cfg->layout == RA_LAYOUT_ZIGZAG && cfg->mask == RA_MASK_CAUSAL;
   if (zz && (cfg->dims.dtype != RA_BF16 || cfg->dims.block_len % 256 != 0))
     return fail(RA_ERR_UNSUPPORTED, "causal zigzag ring backward needs bf16 and block_len %% 256 == 0 (got %d)",
                 cfg->dims.block_len);
-  if (cfg->flags & RA_FLAG_ELIDE_SKIPPED_COPIES)
+  if (full && (cfg->flags & RA_FLAG_ELIDE_SKIPPED_COPIES))
     return fail(RA_ERR_INVALID_ARG, "copy elision does not apply to the full ring");
   RA_CHECK(check_ptr(Q, "Q"));
   RA_CHECK(check_ptr(K, "K"));
@@ -794,6 +893,7 @@ ra_status ra_ring_bwd(const ra_ring_cfg* cfg, const void* Q, const void* K, cons
   if (N > ra::kMaxHostsPerLaunch) return fail(RA_ERR_UNSUPPORTED, "ring backward supports up to %d hosts", ra::kMaxHostsPerLaunch);
   hipStream_t cs = (hipStream_t)compute_stream;
   hipStream_t ms = (cfg->flags & RA_FLAG_SERIALIZE) ? cs : (hipStream_t)comm_stream;
+  if (!full) return ring_bwd_hosts(cfg, Q, K, V, O, lse, dO, dQ, dK, dV, static_cast<char*>(workspace), cs, ms, stats);
   char* ws = static_cast<char*>(workspace);
   float* Dbuf = reinterpret_cast<float*>(ws + w.D);
   char* rk = ws + w.rk;

@@ -218,3 +218,161 @@ def test_ring_fwd_bwd_striped_256k_all_hosts(torch):
         err_k = max(err_k, float(np.abs(got - want_k).max()))
     H.report(f"{w.name} K=0 dK (sampled rows)", tol=TOL_BWD, max_abs=err_k, heads=heads)
     assert err_k <= TOL_BWD
+
+
+# ---------------------------------------------------------------------------
+# one host's share of the backward (a subset of the hosts)
+# ---------------------------------------------------------------------------
+
+def _bwd_hosts(torch, w, q, k, v, O, lse, do, hb, he, flags=0):
+    """ra_ring_bwd for hosts [hb, he): q, O, lse, do hold those hosts' blocks."""
+    import long_context_transformers_amd as ra
+    wh = w.replace(host_begin=hb, host_end=he)
+    cfg = H.cfg_of(wh, flags)
+    dQ = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    dK = torch.empty(k.shape, dtype=torch.float32, device="cuda")
+    dV = torch.empty(v.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(ra.ring_workspace_size(cfg, True), dtype=torch.uint8, device="cuda")
+    st = ra.ring_bwd(cfg, q, k, v, O, lse, do, dQ, dK, dV, ws, torch.cuda.current_stream(), torch.cuda.Stream())
+    torch.cuda.synchronize()
+    return dQ, dK, dV, st
+
+
+SUBSETS = [
+    # (hq, hkv, d, layout, mask, N, c, dtype)
+    (2, 2, 128, C, 1, 4, 130, rs.DT_BF16),
+    (4, 2, 128, S, 1, 3, 192, rs.DT_BF16),
+    (2, 2, 128, rs.LAYOUT_ZIGZAG, 1, 3, 256, rs.DT_BF16),
+    (4, 1, 64, C, 0, 3, 100, rs.DT_BF16),
+    (2, 2, 64, S, 1, 4, 64, rs.DT_F32),
+]
+
+
+@pytest.mark.parametrize("hq,hkv,d,layout,mask,N,c,dtype", SUBSETS)
+def test_ring_bwd_one_host_shares_sum_to_full_ring(torch, hq, hkv, d, layout, mask, N, c, dtype):
+    """Every host's one-host backward: its dQ equals the full ring's dQ of that
+    host bit for bit (same kernels, same step order), and the dK, dV
+    contributions of all hosts sum to the full ring's gradient and to the
+    oracle's.  A two-host range equals the sum of its two one-host runs."""
+    w = rs.Workload("bwd_hosts", 91, 1, hq, hkv, d, N, c, dtype, mask, layout, 0, N)
+    inp = rs.make_inputs(w, with_do=True)
+    q, k, v, do = (H.dev_tensor(x, w.dtype) for x in (inp.q_dev, inp.k_dev, inp.v_dev, inp.do_dev))
+    O, lse, dQf, dKf, dVf, _, _ = _ring_fwd_bwd(torch, w, q, k, v, do)
+    sK = torch.zeros(k.shape, dtype=torch.float64, device="cuda")
+    sV = torch.zeros_like(sK)
+    for h in range(N):
+        dQh, dKh, dVh, st = _bwd_hosts(torch, w, q[h:h + 1], k, v, O[h:h + 1], lse[h:h + 1], do[h:h + 1], h, h + 1)
+        assert torch.equal(dQh[0], dQf[h]), h
+        assert st["transfers"] == N - 1
+        sK += dKh.double()
+        sV += dVh.double()
+    scale = max(1.0, float(dKf.abs().max()), float(dVf.abs().max()))
+    assert float((sK - dKf.double()).abs().max()) <= 1e-5 * scale
+    assert float((sV - dVf.double()).abs().max()) <= 1e-5 * scale
+    tol = TOL_F32 * scale if dtype == rs.DT_F32 else TOL_BWD
+    rows = np.arange(c)
+    _, dKr, dVr = _oracle_grads(w, inp, rows, rows, range(hkv))
+    _compare(f"one-host shares summed {w.name} {layout}/{mask} dK", _gather(sK, rows), dKr, tol)
+    _compare(f"one-host shares summed {w.name} {layout}/{mask} dV", _gather(sV, rows), dVr, tol)
+    if N >= 3:
+        dQ2, dK2, dV2, _ = _bwd_hosts(torch, w, q[1:3], k, v, O[1:3], lse[1:3], do[1:3], 1, 3)
+        assert torch.equal(dQ2, dQf[1:3])
+        d1 = _bwd_hosts(torch, w, q[1:2], k, v, O[1:2], lse[1:2], do[1:2], 1, 2)
+        d2 = _bwd_hosts(torch, w, q[2:3], k, v, O[2:3], lse[2:3], do[2:3], 2, 3)
+        assert float((dK2.double() - d1[1].double() - d2[1].double()).abs().max()) <= 1e-5 * scale
+        assert float((dV2.double() - d1[2].double() - d2[2].double()).abs().max()) <= 1e-5 * scale
+
+
+def _one_host_inputs(torch, w, seed):
+    """Device-drawn bf16 inputs of a one-host workload (Q, dO of the host, the
+    K/V pool), and their float32 copies for the oracle."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    q = torch.randn(rs.q_shape(w, 1), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn(rs.kv_shape(w), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn(rs.kv_shape(w), generator=g, device="cuda").to(torch.bfloat16)
+    do = torch.randn(rs.q_shape(w, 1), generator=g, device="cuda").to(torch.bfloat16)
+    inp = rs.Inputs(q.float().cpu().numpy(), k.float().cpu().numpy(), v.float().cpu().numpy(), None, None, None,
+                    q_host_base=w.host_begin, do_f32=do.float().cpu().numpy())
+    return q, k, v, do, inp
+
+
+def _one_host_fwd_bwd(torch, w, q, k, v, do):
+    O, lse, _ = H.run_ring_fwd(w, None, tensors=(q, k, v))
+    dQ, dK, dV, st = _bwd_hosts(torch, w, q, k, v, O, lse, do, w.host_begin, w.host_end)
+    return O, lse, dQ, dK, dV, st
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name", ["causal_256k_contig", "causal_256k_striped", "striped_786k_gqa"])
+def test_ring_bwd_one_host_share_full_size(torch, name):
+    """One host's share of the backward at full size: the last host of the
+    causal 256K workload (contiguous and striped, 32 heads, c = 32768) and of
+    the 786K striped workload with 32 query heads on 8 KV heads (c = 49152).
+    dQ on 128 seeded rows of every head against the oracle.  For the 256K
+    workloads also K = 0, where every visible score is 0: dQ = 0 exactly, and
+    the host's contribution to dV_k is the sum over its own queries q with
+    t_q >= t_k of dO_q / (t_q + 1), checked on every key row of every head;
+    its contribution to dK_k, scale times the sum over the same queries of
+    (dO_q . v_k - D_q) Q_q / (t_q + 1), on 48 seeded key tokens of 2 heads."""
+    w = rs.workloads()[name]
+    N, c, d, Hq, Hkv = w.n_hosts, w.block_len, w.head_dim, w.heads_q, w.heads_kv
+    print(f"[inputs] drawing {w.name} on the device", flush=True)
+    q, k, v, do, inp = _one_host_inputs(torch, w, 9200 + w.cfg)
+    O, lse, dQ, dK, dV, st = _one_host_fwd_bwd(torch, w, q, k, v, do)
+    assert st["compute_steps"] == N - st["skipped_blocks"] and st["transfers"] == N - 1
+    rows = rs.row_sample(w, 128)
+    desc = cref.row_desc([w.host_begin], range(w.batch), range(Hq), rows)
+    dQr, _, _ = cref.attn_bwd_q_rows(inp.q_f32, inp.k_f32, inp.v_f32, inp.do_f32, n_hosts=N, layout=w.layout,
+                                     causal=w.mask, rows=desc, q_host_base=w.host_begin)
+    _compare(f"one-host ring_bwd {w.name} dQ", _gather(dQ, rows), dQr)
+    if Hq != Hkv:
+        return
+    del O, lse, dQ, dK, dV, inp
+    k.zero_()
+    O, lse, dQ, dK, dV, _ = _one_host_fwd_bwd(torch, w, q, k, v, do)
+    assert int(torch.count_nonzero(dQ)) == 0, "dQ must be exactly zero when K = 0"
+    n = N * c
+    t_all = _token_order(w.layout, N, c)                        # [N, c] token of (host, row)
+    order = np.argsort(t_all.reshape(-1))                       # token -> flat (host, row)
+    tq = t_all[w.host_begin]                                    # tokens of the host's query rows
+    inv = 1.0 / (tq + 1.0)
+    err_v = 0.0
+    for h in range(Hq):
+        wq = do[0, 0, h].double().cpu().numpy() * inv[:, None]  # dO_q / (t_q + 1) at token t_q
+        acc = np.zeros((n, d))
+        acc[tq] = wq
+        want = np.cumsum(acc[::-1], axis=0)[::-1]               # sum over q with t_q >= t_k, token order
+        got = dV[:, 0, h].double().cpu().numpy().reshape(n, d)[order]
+        assert np.all(np.isfinite(got))
+        err_v = max(err_v, float(np.abs(got - want).max()))
+    H.report(f"one-host {w.name} K=0 dV (all rows)", tol=TOL_BWD, max_abs=err_v)
+    assert err_v <= TOL_BWD
+    rng = np.random.default_rng(9800 + w.cfg)
+    scale = 1.0 / np.sqrt(d)
+    err_k = 0.0
+    qsort = np.argsort(tq)[::-1]                                 # the host's rows by descending token
+    for h in sorted(rng.choice(Hq, 2, replace=False).tolist()):
+        Vt = v[:, 0, h].double().cpu().numpy().reshape(n, d)[order]
+        pref = np.cumsum(Vt, axis=0)
+        Qh = q[0, 0, h].double().cpu().numpy()
+        dOh = do[0, 0, h].double().cpu().numpy()
+        Oq = pref[tq] / (tq + 1.0)[:, None]                      # prefix mean of V up to t_q
+        Dq = (dOh * Oq).sum(axis=1)
+        ks = np.sort(np.unique(np.concatenate([[0, n - 1], rng.choice(n, 46, replace=False)])))[::-1]
+        M = np.zeros((d, d))
+        u = np.zeros(d)
+        pos = 0
+        want = np.empty((len(ks), d))
+        for i, kt in enumerate(ks):
+            while pos < len(qsort) and tq[qsort[pos]] >= kt:
+                r = qsort[pos]
+                wr = Qh[r] * inv[r]
+                M += np.outer(wr, dOh[r])
+                u += Dq[r] * wr
+                pos += 1
+            want[i] = scale * (M @ Vt[kt] - u)
+        got = dK[:, 0, h].double().cpu().numpy().reshape(n, d)[order][ks]
+        err_k = max(err_k, float(np.abs(got - want).max()))
+    H.report(f"one-host {w.name} K=0 dK (sampled rows)", tol=TOL_BWD, max_abs=err_k)
+    assert err_k <= TOL_BWD

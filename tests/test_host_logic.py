@@ -226,10 +226,10 @@ def test_ring_argument_checks():
     assert _ring_fwd(_cfg(layout=Z, mask=1, dims=_dims(block_len=64)), big) == L.RA_ERR_UNSUPPORTED
     assert _ring_fwd(_cfg(layout=Z, mask=1, dims=_dims(block_len=256, dtype=1)), big) == L.RA_ERR_UNSUPPORTED
     st = L.RaRingStats()
-    # backward: partial host ranges, and causal zigzag with block_len % 256 != 0,
-    # are not supported
-    assert ra.raw_call("ra_ring_bwd", ctypes.byref(_cfg(host_begin=7)), *([FAKE] * 10), 1 << 40,
-                       None, None, ctypes.byref(st)) == L.RA_ERR_UNSUPPORTED
+    # backward: causal zigzag with block_len % 256 != 0 is not supported;
+    # copy elision only applies to a subset of the hosts
+    assert ra.raw_call("ra_ring_bwd", ctypes.byref(_cfg(flags=1)), *([FAKE] * 10), 1 << 40,
+                       None, None, ctypes.byref(st)) == L.RA_ERR_INVALID_ARG
     assert ra.raw_call("ra_ring_bwd", ctypes.byref(_cfg(layout=Z, mask=1, dims=_dims(block_len=128))),
                        *([FAKE] * 10), 1 << 40, None, None, ctypes.byref(st)) == L.RA_ERR_UNSUPPORTED
     assert ra.raw_call("ra_ring_bwd", ctypes.byref(_cfg(layout=Z, dims=_dims(block_len=63))),
@@ -258,6 +258,24 @@ def test_ring_bwd_fp32_passes_checks():
     rc = ra.raw_call("ra_ring_bwd", ctypes.byref(_cfg(mask=1, dims=_dims(dtype=1))), *([FAKE] * 10), 1 << 40,
                      None, None, ctypes.byref(st))
     assert rc == L.RA_ERR_HIP, (rc, ra.last_error())
+
+
+def test_ring_bwd_host_subset_workspace_and_checks():
+    """One host's share of the backward needs D and the K/V double buffer
+    only (no rotating dK/dV slots); a too-small workspace is refused before
+    any HIP call."""
+    d = _dims(batch=1, heads_q=8, heads_kv=4, head_dim=128, block_len=4096)
+    n = ctypes.c_size_t(0)
+    assert ra.raw_call("ra_ring_workspace_size", ctypes.byref(_cfg(dims=d, host_begin=7, host_end=8)), 1,
+                       ctypes.byref(n)) == 0
+    rows, kv = 8 * 4096, 4 * 4096 * 128
+    assert n.value == rows * 4 + 4 * kv * 2
+    assert ra.raw_call("ra_ring_workspace_size", ctypes.byref(_cfg(dims=d)), 1, ctypes.byref(n)) == 0
+    assert n.value == 8 * (rows * 4 + 4 * kv * 2 + 4 * kv * 4)
+    st = L.RaRingStats()
+    rc = ra.raw_call("ra_ring_bwd", ctypes.byref(_cfg(dims=d, host_begin=7, host_end=8)), *([FAKE] * 10),
+                     rows * 4 + 4 * kv * 2 - 1, None, None, ctypes.byref(st))
+    assert rc == L.RA_ERR_WORKSPACE
 
 
 def test_workspace_size_formula():
