@@ -45,6 +45,10 @@ def lib():
         L.oracle_attn_bwd_q_rows.restype = ci
         L.oracle_attn_bwd_q_rows.argtypes = [_f32p] * 4 + [ci] * 8 + [
             ctypes.c_double, ci, ci, ctypes.c_longlong, _i64p, _f64p, _f64p, _f64p]
+        L.oracle_attn_rows_plain.restype = ci
+        L.oracle_attn_rows_plain.argtypes = L.oracle_attn_rows.argtypes
+        L.oracle_attn_bwd_q_rows_plain.restype = ci
+        L.oracle_attn_bwd_q_rows_plain.argtypes = L.oracle_attn_bwd_q_rows.argtypes
         L.oracle_attn_bwd_kv_rows.restype = ci
         L.oracle_attn_bwd_kv_rows.argtypes = [_f32p] * 4 + [_f64p, _f64p] + [ci] * 8 + [
             ctypes.c_double, ctypes.c_longlong, _i64p, _f64p, _f64p]
@@ -74,10 +78,12 @@ def _f32(a):
 
 
 def attn_rows(q, k, v, *, n_hosts, layout, causal, rows, scale: Optional[float] = None,
-              q_host_base: int = 0):
+              q_host_base: int = 0, plain: bool = False):
     """Forward rows.  q: [nq_hosts][B][Hq][c][d] float32 (host ``h`` at index
     ``h - q_host_base``); k, v: [N][B][Hkv][c][d]; rows: int64 [n, 4] of
-    (host, batch, q_head, local row).  Returns (O [n,d], lse, max, l) fp64."""
+    (host, batch, q_head, local row).  Returns (O [n,d], lse, max, l) fp64.
+    ``plain``: evaluate one row at a time (the per-row form the row sets must
+    match bit for bit; slow on long sequences)."""
     q, k, v = _f32(q), _f32(k), _f32(v)
     nq, B, Hq, c, d = q.shape
     Hkv = k.shape[2]
@@ -86,16 +92,18 @@ def attn_rows(q, k, v, *, n_hosts, layout, causal, rows, scale: Optional[float] 
     rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 4)
     n = rows.shape[0]
     O = np.zeros((n, d)); lse = np.zeros(n); mx = np.zeros(n); l = np.zeros(n)
-    rc = lib().oracle_attn_rows(q, k, v, n_hosts, B, Hq, Hkv, c, d, layout, causal,
-                                float(scale), q_host_base, nq, n, rows, O, lse, mx, l)
+    fn = lib().oracle_attn_rows_plain if plain else lib().oracle_attn_rows
+    rc = fn(q, k, v, n_hosts, B, Hq, Hkv, c, d, layout, causal, float(scale), q_host_base,
+            nq, n, rows, O, lse, mx, l)
     if rc != 0:
         raise ValueError("oracle_attn_rows: bad argument")
     return O, lse, mx, l
 
 
 def attn_bwd_q_rows(q, k, v, do, *, n_hosts, layout, causal, rows, scale=None,
-                    q_host_base: int = 0):
-    """dQ for query rows; also returns the oracle's LSE and D for those rows."""
+                    q_host_base: int = 0, plain: bool = False):
+    """dQ for query rows; also returns the oracle's LSE and D for those rows.
+    ``plain``: one row at a time, as in ``attn_rows``."""
     q, k, v, do = _f32(q), _f32(k), _f32(v), _f32(do)
     nq, B, Hq, c, d = q.shape
     Hkv = k.shape[2]
@@ -104,9 +112,9 @@ def attn_bwd_q_rows(q, k, v, do, *, n_hosts, layout, causal, rows, scale=None,
     rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 4)
     n = rows.shape[0]
     dQ = np.zeros((n, d)); lse = np.zeros(n); D = np.zeros(n)
-    rc = lib().oracle_attn_bwd_q_rows(q, k, v, do, n_hosts, B, Hq, Hkv, c, d, layout,
-                                      causal, float(scale), q_host_base, nq, n, rows, dQ,
-                                      lse, D)
+    fn = lib().oracle_attn_bwd_q_rows_plain if plain else lib().oracle_attn_bwd_q_rows
+    rc = fn(q, k, v, do, n_hosts, B, Hq, Hkv, c, d, layout, causal, float(scale),
+            q_host_base, nq, n, rows, dQ, lse, D)
     if rc != 0:
         raise ValueError("oracle_attn_bwd_q_rows: bad argument")
     return dQ, lse, D

@@ -109,21 +109,15 @@ static size_t idx_row(const or_dims *g, int heads, int host, int b, int h, long 
            (size_t)g->d;
 }
 
-/* Dot product in double.  The definition fixes no summation order; the SIMD
- * reduction lets the compiler split the sum across vector lanes. */
-/* Dot product of two double vectors; 16 partial sums (any order is allowed). */
-static double dot_d(const double *a, const double *b, int d)
+/* Dot product of two double vectors.  The definition fixes no summation
+ * order; the reduction clause lets the compiler split the sum over vector
+ * lanes.  One out-of-line copy, so every caller sums in the same order. */
+__attribute__((noinline)) static double dot_d(const double *a, const double *b, int d)
 {
-    double acc[16] = {0.0};
-    int e = 0;
-    for (; e + 16 <= d; e += 16)
-        for (int u = 0; u < 16; ++u)
-            acc[u] += a[e + u] * b[e + u];
     double s = 0.0;
-    for (; e < d; ++e)
+#pragma omp simd reduction(+ : s)
+    for (int e = 0; e < d; ++e)
         s += a[e] * b[e];
-    for (int u = 0; u < 16; ++u)
-        s += acc[u];
     return s;
 }
 
@@ -138,6 +132,94 @@ static double dot_f32(const float *a, const double *qd, int d)
         s += (double)a[e] * qd[e];
     return s;
 }
+
+/* One query row, the definition written out ([P2] 5.1; [P3] 分块注意力):
+ * the scaled scores of the visible keys and their max, then the exp-sum and
+ * the weighted sum of values, then O = sum / l and LSE = max + ln l.  A row
+ * that sees no key gets O = 0 and LSE = -inf.  sc: N*c doubles of scratch
+ * (the row's scores, kept for the backward). */
+static void fwd_row(const or_dims *g, const double *q, long long r, int qhost, int b,
+                    int kvh, double *sc, double *O, double *mx_out, double *l_out,
+                    double *lse_out)
+{
+    const int d = g->d;
+    const long long c = g->c;
+    const long long tq = token_index(g->layout, g->n_hosts, c, qhost, r);
+    double kd[512];
+    double mx = -INFINITY, l = 0.0;
+    for (int j = 0; j < g->n_hosts; ++j)
+        for (long long rk = 0; rk < c; ++rk) {
+            if (!visible(g->causal, tq, token_index(g->layout, g->n_hosts, c, j, rk)))
+                continue;
+            const float *k = K_ROW(g, j, b, kvh, rk);
+            for (int e = 0; e < d; ++e)
+                kd[e] = (double)k[e];
+            double s = g->scale * dot_d(kd, q, d);
+            sc[j * c + rk] = s;
+            if (s > mx)
+                mx = s;
+        }
+    for (int e = 0; e < d; ++e)
+        O[e] = 0.0;
+    for (int j = 0; j < g->n_hosts; ++j)
+        for (long long rk = 0; rk < c; ++rk) {
+            if (!visible(g->causal, tq, token_index(g->layout, g->n_hosts, c, j, rk)))
+                continue;
+            const float *v = V_ROW(g, j, b, kvh, rk);
+            double p = exp(sc[j * c + rk] - mx);
+            l += p;
+            for (int e = 0; e < d; ++e)
+                O[e] += p * (double)v[e];
+        }
+    *mx_out = mx;
+    if (mx == -INFINITY) {
+        *l_out = 0.0;
+        *lse_out = -INFINITY;
+        return;
+    }
+    for (int e = 0; e < d; ++e)
+        O[e] /= l;
+    *l_out = l;
+    *lse_out = mx + log(l);
+}
+
+/* dQ of one query row after fwd_row: D = dO . O, and over the visible keys
+ * P = exp(s - LSE), dS = P (dO . v - D), dQ = scale * sum dS k. */
+static void bwd_q_row(const or_dims *g, const double *dov, const double *O, long long r,
+                      int qhost, int b, int kvh, const double *sc, double lse, double *D_out,
+                      double *dq)
+{
+    const int d = g->d;
+    const long long c = g->c;
+    const long long tq = token_index(g->layout, g->n_hosts, c, qhost, r);
+    double vd[512];
+    double D = 0.0;
+    for (int e = 0; e < d; ++e)
+        D += dov[e] * O[e];
+    *D_out = D;
+    for (int e = 0; e < d; ++e)
+        dq[e] = 0.0;
+    if (lse == -INFINITY)
+        return;
+    for (int j = 0; j < g->n_hosts; ++j)
+        for (long long rk = 0; rk < c; ++rk) {
+            if (!visible(g->causal, tq, token_index(g->layout, g->n_hosts, c, j, rk)))
+                continue;
+            const float *k = K_ROW(g, j, b, kvh, rk);
+            const float *v = V_ROW(g, j, b, kvh, rk);
+            for (int e = 0; e < d; ++e)
+                vd[e] = (double)v[e];
+            double p = exp(sc[j * c + rk] - lse);
+            double ds = p * (dot_d(vd, dov, d) - D);
+            for (int e = 0; e < d; ++e)
+                dq[e] += g->scale * ds * (double)k[e];
+        }
+}
+
+/* The row-set functions below compute exactly what fwd_row and bwd_q_row
+ * compute, for up to OR_SET rows at once; oracle_attn_rows_plain and
+ * oracle_attn_bwd_q_rows_plain run the per-row forms, and a CPU test checks
+ * that both give bitwise equal results. */
 
 /* Up to OR_SET query rows of one (host, batch, head) are evaluated in one
  * sweep over the keys, so each key/value row is read once per set instead of
@@ -410,6 +492,85 @@ int oracle_attn_bwd_q_rows(const float *Q, const float *K, const float *V,
     }
     free(set_start);
     return 0;
+}
+
+/*
+ * oracle_attn_rows and oracle_attn_bwd_q_rows, one row at a time through
+ * fwd_row and bwd_q_row (same arguments; dQ and D are NULL for the forward).
+ * They exist to check the row-set forms, which must agree with them bit for
+ * bit; they read every key row once per query row, so they suit small inputs.
+ */
+static int rows_plain(const float *Q, const float *K, const float *V, const float *dO,
+                      int n_hosts, int batch, int hq, int hkv, int c, int d, int layout,
+                      int causal, double scale, int q_host_base, int n_q_hosts,
+                      long long n_rows, const long long *rows, double *O, double *lse,
+                      double *mx, double *l, double *dQ, double *D)
+{
+    if (hq <= 0 || hkv <= 0 || hq % hkv != 0 || d <= 0 || d > 512 || c <= 0 || n_hosts <= 0)
+        return -1;
+    or_dims g = {n_hosts, batch, hq, hkv, c, d, layout, causal, scale, K, V};
+    const int group = hq / hkv;
+    for (long long i = 0; i < n_rows; ++i) {
+        const long long *rd = rows + 4 * i;
+        int host = (int)rd[0], b = (int)rd[1], h = (int)rd[2];
+        long long r = rd[3];
+        if (host < 0 || host >= n_hosts || host < q_host_base ||
+            host >= q_host_base + n_q_hosts || b < 0 || b >= batch || h < 0 || h >= hq ||
+            r < 0 || r >= c)
+            return -1;
+    }
+#pragma omp parallel
+    {
+        double *buf = (double *)malloc(sizeof(double) * (3 * (size_t)d + (size_t)n_hosts * c));
+        double *qd = buf, *od = buf + d, *dod = buf + 2 * (size_t)d, *sc = buf + 3 * (size_t)d;
+#pragma omp for schedule(dynamic, 1)
+        for (long long i = 0; i < n_rows; ++i) {
+            const long long *rd = rows + 4 * i;
+            const int host = (int)rd[0], b = (int)rd[1], h = (int)rd[2];
+            const long long r = rd[3];
+            const size_t qo = idx_row(&g, hq, host - q_host_base, b, h, r);
+            for (int e = 0; e < d; ++e)
+                qd[e] = (double)Q[qo + e];
+            double m, den, ls;
+            fwd_row(&g, qd, r, host, b, h / group, sc, O ? O + (size_t)i * d : od, &m, &den,
+                    &ls);
+            if (mx)
+                mx[i] = m;
+            if (l)
+                l[i] = den;
+            lse[i] = ls;
+            if (dQ) {
+                for (int e = 0; e < d; ++e)
+                    dod[e] = (double)dO[qo + e];
+                bwd_q_row(&g, dod, od, r, host, b, h / group, sc, ls, D + i,
+                          dQ + (size_t)i * d);
+            }
+        }
+        free(buf);
+    }
+    return 0;
+}
+
+int oracle_attn_rows_plain(const float *Q, const float *K, const float *V, int n_hosts,
+                           int batch, int hq, int hkv, int c, int d, int layout, int causal,
+                           double scale, int q_host_base, int n_q_hosts, long long n_rows,
+                           const long long *rows, double *O, double *lse, double *mx,
+                           double *l)
+{
+    return rows_plain(Q, K, V, NULL, n_hosts, batch, hq, hkv, c, d, layout, causal, scale,
+                      q_host_base, n_q_hosts, n_rows, rows, O, lse, mx, l, NULL, NULL);
+}
+
+int oracle_attn_bwd_q_rows_plain(const float *Q, const float *K, const float *V,
+                                 const float *dO, int n_hosts, int batch, int hq, int hkv,
+                                 int c, int d, int layout, int causal, double scale,
+                                 int q_host_base, int n_q_hosts, long long n_rows,
+                                 const long long *rows, double *dQ, double *lse_out,
+                                 double *D_out)
+{
+    return rows_plain(Q, K, V, dO, n_hosts, batch, hq, hkv, c, d, layout, causal, scale,
+                      q_host_base, n_q_hosts, n_rows, rows, NULL, lse_out, NULL, NULL, dQ,
+                      D_out);
 }
 
 /*

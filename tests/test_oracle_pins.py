@@ -165,6 +165,27 @@ def test_forward_vs_brute_force(layout, causal, hq, hkv):
         assert abs(mx[n] + math.log(l[n]) - lse[n]) <= 1e-13
 
 
+@pytest.mark.parametrize("layout,causal,hq,hkv,c,d", [
+    (C, 0, 2, 2, 37, 64), (C, 1, 4, 2, 33, 128), (S, 1, 2, 1, 40, 5), (Z, 1, 2, 2, 34, 128)])
+def test_row_sets_equal_per_row_form(layout, causal, hq, hkv, c, d):
+    """The row-set sweeps (up to 16 rows of one head per pass over the keys)
+    reorder only the loop over independent rows: forward outputs, dQ, LSE and
+    D are bitwise equal to the one-row-at-a-time form, for whole sets, ragged
+    tail sets and rows in shuffled order (sets of one)."""
+    N, B = 3, 1
+    q = _rand(71, (N, B, hq, c, d)); k = _rand(72, (N, B, hkv, c, d))
+    v = _rand(73, (N, B, hkv, c, d)); do = _rand(74, (N, B, hq, c, d))
+    rows = _all_rows(N, B, hq, c)
+    shuffled = rows[np.random.default_rng(75).permutation(len(rows))[:40]]
+    for rr in (rows, shuffled):
+        kw = dict(n_hosts=N, layout=layout, causal=causal, rows=rr)
+        for a, b in zip(cref.attn_rows(q, k, v, **kw), cref.attn_rows(q, k, v, plain=True, **kw)):
+            assert np.array_equal(a, b)
+        for a, b in zip(cref.attn_bwd_q_rows(q, k, v, do, **kw),
+                        cref.attn_bwd_q_rows(q, k, v, do, plain=True, **kw)):
+            assert np.array_equal(a, b)
+
+
 def test_single_host_noncausal_is_library_softmax():
     """N = 1, non-causal: plain softmax attention.  Checked against
     scipy.special.softmax and torch's fp64 CPU scaled_dot_product_attention."""
