@@ -567,7 +567,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU: the N virtual hosts of the ring share it; "
+        print(json.dumps({"error": "the ring runs on one GPU: its N virtual hosts share it; "
                                    "--gpus above 1 is not supported", "n_gpus": args.gpus}))
         sys.exit(2)
 

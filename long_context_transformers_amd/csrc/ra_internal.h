@@ -1,4 +1,4 @@
-// ra_internal.h -- declarations shared by the host driver (ra_host.cpp) and
+// ra_internal.h -- declarations shared by the host driver (ra_host.hip) and
 // the HIP kernels (ra_fwd.hip, ra_bwd.hip, ra_elem.hip).  Not part of the ABI.
 #pragma once
 #include <hip/hip_runtime.h>

@@ -23,8 +23,8 @@ def golden_dir():
 
 def pytest_terminal_summary(terminalreporter, exitstatus, config):
     """Parity margins of the GPU tests that ran: the worst checks (max error
-    over tolerance), and every check as JSON in $RA_PARITY_JSON or
-    gpurun_out/parity_margins.json when that folder exists."""
+    over tolerance), and every check as JSON in the file $RA_PARITY_JSON
+    names, when it is set."""
     import json
     helpers = sys.modules.get("tests.gpu_helpers")
     rows = list(getattr(helpers, "MARGINS", []) or [])
@@ -39,8 +39,6 @@ def pytest_terminal_summary(terminalreporter, exitstatus, config):
         tr.write_line(f"{r['ratio']:.3f}  {r['name']}  err={r['err']:.2e} tol={r['tol']:.0e}")
     tr.write_line(f"{len(rows)} parity checks recorded; worst ratio {rows[0]['ratio']:.3f}")
     out = os.environ.get("RA_PARITY_JSON")
-    if not out and os.path.isdir(os.path.join(ROOT, "gpurun_out")):
-        out = os.path.join(ROOT, "gpurun_out", "parity_margins.json")
     if out:
         with open(out, "w") as f:
             json.dump(rows, f, indent=1)
