@@ -146,8 +146,6 @@ void fwd_bf16_kernel(FwdArgs a) {
   const __bf16* vp = reinterpret_cast<const __bf16*>(a.v) + host * a.kv_host_stride +
                      ((int64_t)(b * a.hkv + kvh) * c) * D;
   const __amdgpu_buffer_rsrc_t rq = tile::rsrc(qp, blk_bytes);
-  const __amdgpu_buffer_rsrc_t rk = tile::rsrc(kp, blk_bytes);
-  const __amdgpu_buffer_rsrc_t rv = tile::rsrc(vp, blk_bytes);
   float* mp = a.m + host * a.ml_host_stride + (int64_t)(b * a.hq + head) * c;
   float* lp = a.l + host * a.ml_host_stride + (int64_t)(b * a.hq + head) * c;
   float* op = a.o + host * a.q_host_stride + ((int64_t)(b * a.hq + head) * c) * D;
