@@ -287,12 +287,12 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int mt = 1; mt < 4; ++mt)
         mx = fmaxf(mx, fmaxf(fmaxf(s[mt][qs][0], s[mt][qs][1]), fmaxf(s[mt][qs][2], s[mt][qs][3])));
-      mx = allmax(mx) * c2;
-      m_true[qs] = fmaxf(m_true[qs], mx);
+      mx *= c2;                              // this lane's max over its 16 keys
+      m_true[qs] = fmaxf(m_true[qs], mx);    // lane-local; reduced over the row on exit
       // move the reference max (rescaling O and l) only when some row's max
-      // grew past the threshold
+      // grew past the threshold; the row max is formed only then
       if (__builtin_amdgcn_ballot_w64(mx > m_ref[qs] + kRescaleThreshold)) {
-        const float m_new = fmaxf(m_ref[qs], mx);
+        const float m_new = fmaxf(m_ref[qs], allmax(mx));
         const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_ref[qs] - m_new);
         lh[qs] *= alpha;
 #pragma unroll
@@ -344,6 +344,7 @@ void fwd_bf16_kernel(FwdArgs a) {
   // ---- write the state back, referenced to the true running max ----
 #pragma unroll
   for (int qs = 0; qs < 2; ++qs) {
+    m_true[qs] = allmax(m_true[qs]);
     const float fix = (m_true[qs] == -INFINITY || m_ref[qs] == m_true[qs]) ? 1.f : exp2f(m_ref[qs] - m_true[qs]);
     const float l_tot = allsum(lh[qs] * fix);
     const int qr = qw0 + 16 * qs + l16;
