@@ -19,9 +19,11 @@
 //    one head, or 32 rows of up to 4 heads that share a key/value head
 //    (grouped heads), so one K/V tile in LDS feeds all of them.
 //  * Scores are computed transposed, S^T = K Q^T: the MFMA result puts one
-//    query row per lane column (lane % 16) and 4 keys per lane group, so the
-//    row max and row sum are in-lane over 16 keys plus two exchanges across
-//    the lane groups (v_permlane16_swap, v_permlane32_swap).
+//    query row per lane column (lane % 16) and 4 keys per lane group, so a
+//    row's max and sum are in-lane over 16 keys plus two exchanges across
+//    the lane groups (v_permlane16_swap, v_permlane32_swap).  Per tile each
+//    lane only checks its own max against the reference; the exchange runs
+//    when the lazy rescale fires, and once per row on exit.
 //  * Q stays in registers for the whole block (B operand of S^T).  K and V
 //    tiles of 64 keys travel HBM -> LDS by LDS-DMA into unpadded, swizzled
 //    row-major tiles (ra_tile.h): K is read by rows (A operand of S^T), V by
