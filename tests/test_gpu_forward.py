@@ -86,6 +86,52 @@ def test_block_fwd_ring_order_small(torch, dtype, d, hq, hkv, layout, mask, N, c
            lse.cpu().numpy().reshape(-1).astype(np.float64), O_ref, lse_ref)
 
 
+@pytest.mark.parametrize("layout,mask", [(C, 0), (C, 1), (S, 1)])
+def test_block_fwd_growing_logits(torch, layout, mask):
+    """Keys scaled up with their token index (x0.5 .. x6) and Q x 2, so a
+    row's running max keeps climbing across the key tiles and the lazy
+    rescale fires again and again along the ring; all rows against the
+    oracle at the bf16 tolerances."""
+    import long_context_transformers_amd as ra
+    N, c, d, hq, hkv = 3, 320, 128, 2, 2
+    w = rs.Workload("growing", 92, 1, hq, hkv, d, N, c, rs.DT_BF16, mask, layout, 0, N, q_scale=2.0)
+    inp = rs.make_inputs(w)
+    S_len = N * c
+    for h in range(N):
+        t = np.array([npref.token_index(layout, N, c, h, r) for r in range(c)], dtype=np.float32)
+        f = (0.5 + 5.5 * t / S_len).astype(np.float32)
+        bits = rs.f32_to_bf16_bits(inp.k_f32[h] * f[None, None, :, None])
+        inp.k_dev[h] = bits
+        inp.k_f32[h] = rs.bf16_bits_to_f32(bits)
+    dims = H.dims_of(w)
+    q, k, v = (H.dev_tensor(x, w.dtype) for x in (inp.q_dev, inp.k_dev, inp.v_dev))
+    rows_all = cref.row_desc(range(N), range(w.batch), range(hq), range(c))
+    O_ref, lse_ref, _, _ = cref.attn_rows(inp.q_f32, inp.k_f32, inp.v_f32, n_hosts=N, layout=layout,
+                                          causal=mask, rows=rows_all)
+    # within a block the keys' scale grows tile by tile: the row max of the
+    # last 64-key tile of host 0's block exceeds that of its first tile by far
+    # more than the rescale threshold (8 in log2 units) on most rows
+    s0 = np.einsum("hrd,hkd->hrk", inp.q_f32[0, 0].astype(np.float64),
+                   inp.k_f32[0, 0].astype(np.float64)) / np.sqrt(d) * 1.4426950408889634
+    grow = s0[:, :, -64:].max(axis=2) - s0[:, :, :64].max(axis=2)
+    assert np.median(grow) > 8
+    O_out = torch.empty((N, w.batch, hq, c, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((N, w.batch, hq, c), dtype=torch.float32, device="cuda")
+    for i in range(N):
+        m = torch.empty((w.batch, hq, c), dtype=torch.float32, device="cuda")
+        l = torch.empty_like(m)
+        O = torch.empty((w.batch, hq, c, d), dtype=torch.float32, device="cuda")
+        ra.state_init(dims, m, l, O)
+        for st in ra.schedule(N, i, c, layout, mask):
+            ra.block_fwd(dims, q[i], k[st["src"]], v[st["src"]], mask, st["q_offset"],
+                         st["kv_offset"], st["stride"], m, l, O)
+        ra.finalize(dims, m, l, O, O_out[i], lse[i])
+    torch.cuda.synchronize()
+    _check(f"block_fwd growing logits {layout=} {mask=}", w,
+           O_out.float().cpu().numpy().reshape(-1, d).astype(np.float64),
+           lse.cpu().numpy().reshape(-1).astype(np.float64), O_ref, lse_ref)
+
+
 def test_block_fwd_any_order_and_empty_rows(torch):
     """Order invariance on the GPU, and a striped strict block alone leaves
     row 0 (no visible key) at the initial state without NaN."""
