@@ -120,12 +120,16 @@ def test_ring_bwd_striped_causal_4096_gqa_sampled(torch):
 
 
 def _token_order(layout, N, c):
-    """t[h, r] = token index of local row r on host h (contiguous or striped),
-    pinned against the oracle's token map on a few rows."""
+    """t[h, r] = token index of local row r on host h (contiguous, striped or
+    zigzag), pinned against the oracle's token map on a few rows."""
     r = np.arange(c, dtype=np.int64)[None, :]
     h = np.arange(N, dtype=np.int64)[:, None]
-    t = r * N + h if layout == S else h * c + r
-    for hh, rr in ((0, 0), (N - 1, c - 1), (1, c // 2), (N // 2, 7)):
+    if layout == rs.LAYOUT_ZIGZAG:
+        half = c // 2
+        t = np.where(r < half, h * half + r, (2 * N - 1 - h) * half + (r - half))
+    else:
+        t = r * N + h if layout == S else h * c + r
+    for hh, rr in ((0, 0), (N - 1, c - 1), (1, c // 2), (N // 2, 7), (0, c // 2 - 1), (N - 1, c // 2)):
         assert t[hh, rr] == cref.token_index(layout, N, c, hh, rr)
     return t
 
@@ -304,10 +308,12 @@ def _one_host_fwd_bwd(torch, w, q, k, v, do):
 
 
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("name", ["causal_256k_contig", "causal_256k_striped", "striped_786k_gqa"])
+@pytest.mark.parametrize("name", ["causal_256k_contig", "causal_256k_striped", "causal_256k_zigzag",
+                                  "striped_786k_gqa"])
 def test_ring_bwd_one_host_share_full_size(torch, name):
     """One host's share of the backward at full size: the last host of the
-    causal 256K workload (contiguous and striped, 32 heads, c = 32768) and of
+    causal 256K workload (contiguous, striped and zigzag, 32 heads,
+    c = 32768) and of
     the 786K striped workload with 32 query heads on 8 KV heads (c = 49152).
     dQ on 128 seeded rows of every head against the oracle.  For the 256K
     workloads also K = 0, where every visible score is 0: dQ = 0 exactly, and
